@@ -1,0 +1,158 @@
+"""Python binding over the C ABI, named like the C entry points.
+
+Argument marshalling only: torch tensors supply device pointers and the current
+HIP stream; every step of the computation runs in the HIP kernels of libattn.so.
+Shapes are read from the tensors; the library re-validates everything.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16, torch.float32: _lib.ATTN_F32}
+_LAYOUT = {"bshd": _lib.ATTN_BSHD, "bhsd": _lib.ATTN_BHSD}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_lib.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int):
+    if status != _lib.ATTN_OK:
+        raise AttnError(status, _lib.last_error())
+
+
+def _need(t: torch.Tensor, name: str, dtypes=None, contiguous=True):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool,
+                     block_table: Optional[torch.Tensor] = None,
+                     seqlens_k: Optional[torch.Tensor] = None, seqlen_k: Optional[int] = None,
+                     layout: str = "bshd", out: Optional[torch.Tensor] = None,
+                     out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
+                     scale: float = 0.0, precise: bool = False, stream=None) -> torch.Tensor:
+    """Tiled attention forward. q: [B,S_q,Hq,d] (bshd) or [B,Hq,S_q,d] (bhsd).
+
+    Paged K/V (block_table given): k, v are [num_blocks, 64, Hkv, d] caches and
+    seqlens_k [B] int32 is required; ``seqlen_k`` (host-side bound) defaults to
+    64 * block_table.shape[1]. Dense K/V: k, v in the layout of q.
+    """
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    _need(k, "k", (q.dtype,))
+    _need(v, "v", (q.dtype,))
+    if layout not in _LAYOUT:
+        raise ValueError("layout must be 'bshd' or 'bhsd'")
+    if q.dim() != 4:
+        raise ValueError("q must be 4-D")
+    if layout == "bshd":
+        B, Sq, Hq, d = q.shape
+    else:
+        B, Hq, Sq, d = q.shape
+    paged = block_table is not None
+    if paged:
+        _need(block_table, "block_table", (torch.int32,))
+        if seqlens_k is None:
+            raise ValueError("paged K/V needs seqlens_k")
+        num_blocks, page, Hkv = k.shape[0], k.shape[1], k.shape[2]
+        if page != _lib.ATTN_PAGE_SIZE:
+            raise ValueError(f"pages must hold {_lib.ATTN_PAGE_SIZE} tokens")
+        max_blocks = block_table.shape[1]
+        Sk = seqlen_k if seqlen_k is not None else max_blocks * _lib.ATTN_PAGE_SIZE
+    else:
+        num_blocks = max_blocks = 0
+        if layout == "bshd":
+            Sk, Hkv = k.shape[1], k.shape[2]
+        else:
+            Hkv, Sk = k.shape[1], k.shape[2]
+        if seqlen_k is not None and seqlen_k != Sk:
+            raise ValueError("dense K/V: seqlen_k must equal the K/V row count")
+    if seqlens_k is not None:
+        _need(seqlens_k, "seqlens_k", (torch.int32,))
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out", tuple(_DT))
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,))
+    a = _lib.PrefillArgs(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(block_table), _ptr(seqlens_k),
+        B, Hq, Hkv, Sq, Sk, d, num_blocks, max_blocks, _DT[q.dtype], _DT[out.dtype],
+        _LAYOUT[layout], int(bool(causal)), int(bool(precise)), float(scale))
+    _check(_lib.load().attn_prefill_fwd(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def attn_decode_workspace_bytes(batch: int, num_heads_q: int, num_splits: int, head_dim: int) -> int:
+    return int(_lib.load().attn_decode_workspace_bytes(batch, num_heads_q, num_splits, head_dim))
+
+
+def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_table: torch.Tensor, seqlens_k: torch.Tensor, *, max_seqlen_k: int,
+                    num_splits: int, out: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, scale: float = 0.0,
+                    stream=None) -> torch.Tensor:
+    """Split-KV decode. q: [B, Hq, d] (or any shape with B*Hq*d elements in that order)."""
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    _need(k_cache, "k_cache", (q.dtype,))
+    _need(v_cache, "v_cache", (q.dtype,))
+    _need(block_table, "block_table", (torch.int32,))
+    _need(seqlens_k, "seqlens_k", (torch.int32,))
+    num_blocks, page, Hkv, d = k_cache.shape
+    if page != _lib.ATTN_PAGE_SIZE:
+        raise ValueError(f"pages must hold {_lib.ATTN_PAGE_SIZE} tokens")
+    B = block_table.shape[0]
+    Hq = q.numel() // (B * d) if B else 0
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    need = attn_decode_workspace_bytes(B, Hq, num_splits, d) if B else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    a = _lib.DecodeArgs(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
+        _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        B, Hq, Hkv, d, num_blocks, block_table.shape[1], int(max_seqlen_k), int(num_splits),
+        _DT[q.dtype], _DT[out.dtype], float(scale))
+    _check(_lib.load().attn_decode_fwd(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def attn_splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, *,
+                         out: Optional[torch.Tensor] = None, out_dtype=torch.float32,
+                         lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Merge partials: partial_o [B, H, S, d] fp32, partial_lse [B, H, S] fp32 -> [B, H, d]."""
+    _need(partial_o, "partial_o", (torch.float32,))
+    _need(partial_lse, "partial_lse", (torch.float32,))
+    B, H, S, d = partial_o.shape
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype, device=partial_o.device)
+    a = _lib.CombineArgs(_ptr(partial_o), _ptr(partial_lse), _ptr(out), _ptr(lse), B, H, S, d,
+                         _DT[out.dtype])
+    _check(_lib.load().attn_splitkv_combine(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,257 @@
+// C ABI of libattn.so: argument validation, launch-shape selection, error reporting.
+// Every entry point validates on the host before touching the HIP runtime, returns a
+// status code and never lets a C++ exception escape.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+attn_status_t ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool valid_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+attn_status_t device_ready() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_NO_DEVICE, "no HIP device is available");
+  }
+  return ATTN_OK;
+}
+
+attn_status_t launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t attn_device_count(void) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
+  try {
+    if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+    if (a->batch < 0 || a->seqlen_q < 0) return fail(ATTN_ERR_INVALID_ARG, "batch and seqlen_q must be >= 0");
+    if (a->qkv_dtype != ATTN_F16 && a->qkv_dtype != ATTN_BF16)
+      return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
+    if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
+      return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+    if (a->layout != ATTN_BSHD && a->layout != ATTN_BHSD)
+      return fail(ATTN_ERR_INVALID_ARG, "layout must be ATTN_BSHD or ATTN_BHSD");
+    if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (a->precise != 0 && a->precise != 1) return fail(ATTN_ERR_INVALID_ARG, "precise must be 0 or 1");
+    if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
+    if (a->num_heads_q <= 0 || a->num_heads_kv <= 0)
+      return fail(ATTN_ERR_INVALID_ARG, "head counts must be positive");
+    if (a->num_heads_q % a->num_heads_kv != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
+                  a->num_heads_q, a->num_heads_kv);
+    const int G = a->num_heads_q / a->num_heads_kv;
+    if (G > 128) return fail(ATTN_ERR_UNSUPPORTED, "GQA ratio %d above 128 is not supported", G);
+    if (a->seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "seqlen_k must be >= 0");
+    if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    if (a->batch > kMaxGridYZ || a->num_heads_kv > kMaxGridYZ)
+      return fail(ATTN_ERR_UNSUPPORTED, "batch and num_heads_kv must be <= %lld", (long long)kMaxGridYZ);
+    const bool paged = a->block_table != nullptr;
+    if (paged) {
+      if (!a->seqlens_k) return fail(ATTN_ERR_INVALID_ARG, "paged K/V requires seqlens_k");
+      if (a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "paged K/V requires num_blocks > 0 and max_blocks_per_seq > 0");
+      if ((int64_t)a->max_blocks_per_seq * ATTN_PAGE_SIZE < a->seqlen_k)
+        return fail(ATTN_ERR_INVALID_ARG, "block table holds %lld keys, fewer than seqlen_k = %d",
+                    (long long)a->max_blocks_per_seq * ATTN_PAGE_SIZE, a->seqlen_k);
+      if (!aligned4(a->block_table)) return fail(ATTN_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    }
+    if (a->seqlens_k && !aligned4(a->seqlens_k)) return fail(ATTN_ERR_INVALID_ARG, "seqlens_k must be 4-byte aligned");
+    if (a->batch == 0 || a->seqlen_q == 0) return ok();
+    if (!a->q || !a->k || !a->v || !a->o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+    if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+      return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (a->lse && !aligned4(a->lse)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+
+    const int64_t D = a->head_dim, Sq = a->seqlen_q, Sk = a->seqlen_k;
+    const int64_t Hq = a->num_heads_q, Hkv = a->num_heads_kv;
+    attn::PrefillParams p{};
+    p.q = static_cast<const uint16_t*>(a->q);
+    p.k = static_cast<const uint16_t*>(a->k);
+    p.v = static_cast<const uint16_t*>(a->v);
+    p.o = a->o;
+    p.lse = a->lse;
+    p.block_table = a->block_table;
+    p.seqlens_k = a->seqlens_k;
+    if (a->layout == ATTN_BSHD) {
+      p.q_sb = Sq * Hq * D; p.q_sh = D; p.q_ss = Hq * D;
+      p.kv_sb = Sk * Hkv * D; p.kv_sh = D; p.kv_ss = Hkv * D;
+    } else {
+      p.q_sb = Hq * Sq * D; p.q_sh = Sq * D; p.q_ss = D;
+      p.kv_sb = Hkv * Sk * D; p.kv_sh = Sk * D; p.kv_ss = D;
+    }
+    p.o_sb = p.q_sb; p.o_sh = p.q_sh; p.o_ss = p.q_ss;
+    p.batch = a->batch; p.hq = a->num_heads_q; p.hkv = a->num_heads_kv; p.group = G;
+    p.seqlen_q = a->seqlen_q; p.seqlen_k = a->seqlen_k;
+    p.num_blocks = a->num_blocks; p.max_blocks = a->max_blocks_per_seq;
+    p.bq = 128 / G;
+    p.causal = a->causal; p.o_dtype = a->o_dtype;
+    const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+
+    if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
+    return launch_status(attn::launch_prefill(p, a->head_dim, a->qkv_dtype, a->precise != 0,
+                                              static_cast<hipStream_t>(stream)),
+                         "prefill");
+  } catch (...) {
+    return fail(ATTN_ERR_LAUNCH, "internal error in attn_prefill_fwd");
+  }
+}
+
+size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_heads_q, int32_t num_splits,
+                                   int32_t head_dim) {
+  if (batch <= 0 || num_heads_q <= 0 || num_splits <= 0 || num_splits > ATTN_MAX_SPLITS || !valid_d(head_dim))
+    return 0;
+  const size_t rows = (size_t)batch * num_heads_q * num_splits;
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+attn_status_t attn_splitkv_combine(const attn_combine_args_t* a, void* stream) {
+  try {
+    if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+    if (a->batch < 0 || a->num_heads < 0) return fail(ATTN_ERR_INVALID_ARG, "batch and num_heads must be >= 0");
+    if (a->num_splits < 1 || a->num_splits > ATTN_MAX_SPLITS)
+      return fail(ATTN_ERR_INVALID_ARG, "num_splits must be in [1, %d]", ATTN_MAX_SPLITS);
+    if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256");
+    if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
+      return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+    const int64_t pairs = (int64_t)a->batch * a->num_heads;
+    if (pairs == 0) return ok();
+    if (pairs > (int64_t)1 << 30) return fail(ATTN_ERR_UNSUPPORTED, "batch * num_heads too large");
+    if (!a->partial_o || !a->partial_lse || !a->o)
+      return fail(ATTN_ERR_INVALID_ARG, "partial_o, partial_lse and o must be non-NULL");
+    if (!aligned4(a->partial_o) || !aligned4(a->partial_lse) || !aligned4(a->o) || (a->lse && !aligned4(a->lse)))
+      return fail(ATTN_ERR_INVALID_ARG, "buffers must be 4-byte aligned");
+    attn::CombineParams p{};
+    p.part_o = a->partial_o; p.part_lse = a->partial_lse; p.o = a->o; p.lse = a->lse;
+    p.pairs = (int32_t)pairs; p.num_splits = a->num_splits; p.o_dtype = a->o_dtype;
+    if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
+    return launch_status(attn::launch_combine(p, a->head_dim, static_cast<hipStream_t>(stream)), "combine");
+  } catch (...) {
+    return fail(ATTN_ERR_LAUNCH, "internal error in attn_splitkv_combine");
+  }
+}
+
+attn_status_t attn_decode_fwd(const attn_decode_args_t* a, void* stream) {
+  try {
+    if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+    if (a->batch < 0) return fail(ATTN_ERR_INVALID_ARG, "batch must be >= 0");
+    if (a->qkv_dtype != ATTN_F16 && a->qkv_dtype != ATTN_BF16)
+      return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
+    if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
+      return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+    if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
+    if (a->num_heads_q <= 0 || a->num_heads_kv <= 0)
+      return fail(ATTN_ERR_INVALID_ARG, "head counts must be positive");
+    if (a->num_heads_q % a->num_heads_kv != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
+                  a->num_heads_q, a->num_heads_kv);
+    const int G = a->num_heads_q / a->num_heads_kv;
+    if (G > 16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports GQA ratios up to 16 (got %d)", G);
+    if (a->num_splits < 1 || a->num_splits > ATTN_MAX_SPLITS)
+      return fail(ATTN_ERR_INVALID_ARG, "num_splits must be in [1, %d]", ATTN_MAX_SPLITS);
+    if (a->max_seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_k must be >= 0");
+    if (a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
+      return fail(ATTN_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be positive");
+    if ((int64_t)a->max_blocks_per_seq * ATTN_PAGE_SIZE < a->max_seqlen_k)
+      return fail(ATTN_ERR_INVALID_ARG, "block table holds %lld keys, fewer than max_seqlen_k = %d",
+                  (long long)a->max_blocks_per_seq * ATTN_PAGE_SIZE, a->max_seqlen_k);
+    if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    if (a->batch > kMaxGridYZ || a->num_heads_kv > kMaxGridYZ)
+      return fail(ATTN_ERR_UNSUPPORTED, "batch and num_heads_kv must be <= %lld", (long long)kMaxGridYZ);
+    if (a->batch == 0) return ok();
+    if (!a->q || !a->k_cache || !a->v_cache || !a->o || !a->block_table || !a->seqlens_k || !a->workspace)
+      return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seqlens_k, o and workspace must be non-NULL");
+    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned4(a->o))
+      return fail(ATTN_ERR_INVALID_ARG, "q, k_cache and v_cache must be 16-byte aligned, o 4-byte aligned");
+    if (!aligned4(a->block_table) || !aligned4(a->seqlens_k) || (a->lse && !aligned4(a->lse)))
+      return fail(ATTN_ERR_INVALID_ARG, "block_table, seqlens_k and lse must be 4-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t need = attn_decode_workspace_bytes(a->batch, a->num_heads_q, a->num_splits, a->head_dim);
+    if (a->workspace_bytes < need)
+      return fail(ATTN_ERR_INVALID_ARG, "workspace has %zu bytes, needs %zu", a->workspace_bytes, need);
+
+    const int64_t rows = (int64_t)a->batch * a->num_heads_q * a->num_splits;
+    float* part_o = static_cast<float*>(a->workspace);
+    float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) +
+                                               align256((size_t)rows * a->head_dim * sizeof(float)));
+    int part = (a->max_seqlen_k + a->num_splits - 1) / a->num_splits;
+    part = ((part + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE) * ATTN_PAGE_SIZE;
+    if (part == 0) part = ATTN_PAGE_SIZE;
+
+    attn::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(a->q);
+    p.k = static_cast<const uint16_t*>(a->k_cache);
+    p.v = static_cast<const uint16_t*>(a->v_cache);
+    p.block_table = a->block_table; p.seqlens_k = a->seqlens_k;
+    p.part_o = part_o; p.part_lse = part_lse;
+    p.batch = a->batch; p.hq = a->num_heads_q; p.hkv = a->num_heads_kv; p.group = G;
+    p.num_blocks = a->num_blocks; p.max_blocks = a->max_blocks_per_seq;
+    p.max_seqlen_k = a->max_seqlen_k; p.num_splits = a->num_splits; p.part_tokens = part;
+    const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+
+    attn::CombineParams c{};
+    c.part_o = part_o; c.part_lse = part_lse; c.o = a->o; c.lse = a->lse;
+    c.pairs = a->batch * a->num_heads_q; c.num_splits = a->num_splits; c.o_dtype = a->o_dtype;
+
+    if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (attn_status_t st = launch_status(attn::launch_decode_split(p, a->head_dim, a->qkv_dtype, s), "decode split");
+        st != ATTN_OK)
+      return st;
+    return launch_status(attn::launch_combine(c, a->head_dim, s), "decode combine");
+  } catch (...) {
+    return fail(ATTN_ERR_LAUNCH, "internal error in attn_decode_fwd");
+  }
+}
+
+}  // extern "C"

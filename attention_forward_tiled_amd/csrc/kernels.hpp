@@ -1,0 +1,58 @@
+// Kernel parameter blocks and launchers (internal to libattn.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+enum DType { kF16 = 0, kBF16 = 1, kF32 = 2 };
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  const int32_t* block_table;   // null for dense K/V
+  const int32_t* seqlens_k;     // null: every sequence has seqlen_k keys
+  int64_t q_sb, q_sh, q_ss;     // element strides of Q over (batch, head, position)
+  int64_t o_sb, o_sh, o_ss;     // same for O (elements of o_dtype)
+  int64_t kv_sb, kv_sh, kv_ss;  // dense K/V strides over (batch, kv head, position)
+  int32_t batch, hq, hkv, group, seqlen_q, seqlen_k;
+  int32_t num_blocks, max_blocks;
+  int32_t bq;                   // query positions per workgroup (rows = group * bq <= 128)
+  int32_t causal, o_dtype;
+  float scale_log2;             // softmax scale * log2(e)
+};
+
+struct DecodeParams {
+  const uint16_t* q;            // [B, Hq, d]
+  const uint16_t* k;            // [num_blocks, 64, Hkv, d]
+  const uint16_t* v;
+  const int32_t* block_table;   // [B, max_blocks]
+  const int32_t* seqlens_k;     // [B]
+  float* part_o;                // [B, Hq, num_splits, d]
+  float* part_lse;              // [B, Hq, num_splits]
+  int32_t batch, hq, hkv, group;
+  int32_t num_blocks, max_blocks, max_seqlen_k, num_splits;
+  int32_t part_tokens;          // keys per split (multiple of 64)
+  float scale_log2;
+};
+
+struct CombineParams {
+  const float* part_o;          // [B*H, S, d]
+  const float* part_lse;        // [B*H, S]
+  void* o;                      // [B*H, d]
+  float* lse;                   // optional [B*H]
+  int32_t pairs, num_splits, o_dtype;
+};
+
+// Each launcher returns hipSuccess or the launch error; shapes were validated by the caller.
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int qkv_dtype, bool precise,
+                          hipStream_t stream);
+hipError_t launch_decode_split(const DecodeParams& p, int head_dim, int qkv_dtype,
+                               hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace attn

@@ -1,18 +1,23 @@
 """Seeded input generation (numpy, host memory).
 
-Values are drawn as float32 N(0,1) from ``numpy.random.Generator(PCG64(seed))``,
-multiplied by the case's exact power-of-two ``value_scale`` and rounded
-(round-to-nearest-even) to the storage dtype. Arrays hold the raw 16-bit
-storage patterns (``uint16``); ``bits_to_f64`` upcasts them exactly.
+Values are float32 N(0,1) draws, multiplied by the case's exact power-of-two
+``value_scale`` and rounded (round-to-nearest-even) to the storage dtype. Arrays
+hold the raw 16-bit storage patterns (``uint16``); ``bits_to_f64`` upcasts them
+exactly.
 
-Draw order for a prefill case: Q, K, V (each in logical BSHD order), then the
-page permutation. For a decode case: key lengths, Q, the K page pool, the V
-page pool, then the page permutation. Storage slots past a sequence's last key
-are filled with NaN when ``poison`` is set, so a kernel that lets them reach
-the output fails parity.
+Streams: every array has a stream id (Q = 1, K = 2, V = 3); its elements, in
+C order, are cut into chunks of 2^22 and chunk i is drawn from
+``Generator(PCG64(SeedSequence([seed, stream, i])))``, so large arrays fill in
+parallel threads yet depend only on the seed. Integer structure (decode key
+lengths, then the page permutation) comes from ``PCG64(SeedSequence([seed, 0]))``.
+Prefill Q/K/V are drawn in logical BSHD order whatever the storage. Storage
+slots past a sequence's last key are filled with NaN when ``poison`` is set,
+so a kernel that lets them reach the output fails parity.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional
 
@@ -21,7 +26,7 @@ import numpy as np
 from .configs import PAGE, DecodeCase, PrefillCase
 
 NAN_BITS = {"f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
-_CHUNK = 1 << 24
+_CHUNK = 1 << 22
 
 
 def round_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -52,16 +57,33 @@ def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     return bits_to_f32(bits, dtype).astype(np.float64)
 
 
-def _normal_bits(rng: np.random.Generator, shape, dtype: str, scale: float) -> np.ndarray:
-    """Draw N(0,1)*scale in float32, chunk by chunk, and round to the storage dtype."""
+def _bf16_bits_inplace(x: np.ndarray) -> np.ndarray:
+    """RTNE float32 -> bf16 for finite values, reusing x's buffer."""
+    u = x.view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal_bits(seed: int, stream: int, shape, dtype: str, scale: float) -> np.ndarray:
+    """Draw N(0,1)*scale in float32 chunk by chunk (threads) and round to the storage dtype."""
     out = np.empty(int(np.prod(shape)), dtype=np.uint16)
     n = out.size
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
+
+    def fill(i):
+        s, e = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, i])))
         x = rng.standard_normal(e - s, dtype=np.float32)
         if scale != 1.0:
             x *= np.float32(scale)
-        out[s:e] = round_to_bits(x, dtype)
+        out[s:e] = _bf16_bits_inplace(x) if dtype == "bf16" else round_to_bits(x, dtype)
+
+    n_chunks = -(-n // _CHUNK)
+    if n_chunks <= 1:
+        for i in range(n_chunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, n_chunks)) as ex:
+            list(ex.map(fill, range(n_chunks)))
     return out.reshape(shape)
 
 
@@ -90,14 +112,14 @@ class DecodeInputs:
 
 
 def make_prefill_inputs(case: PrefillCase, seed: int = 0) -> PrefillInputs:
-    rng = np.random.Generator(np.random.PCG64(seed))
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0])))
     B, Sq, Sk, Hq, Hkv, d = case.batch, case.seqlen_q, case.seqlen_k, case.heads_q, case.heads_kv, case.head_dim
     lens = np.asarray(case.lengths(), dtype=np.int32)
     if lens.shape != (B,) or (lens < 0).any() or (lens > Sk).any():
         raise ValueError("seqlens_k must have one entry per sequence, each in [0, seqlen_k]")
-    q = _normal_bits(rng, (B, Sq, Hq, d), case.dtype, case.value_scale)
-    k = _normal_bits(rng, (B, Sk, Hkv, d), case.dtype, case.value_scale)
-    v = _normal_bits(rng, (B, Sk, Hkv, d), case.dtype, case.value_scale)
+    q = _normal_bits(seed, 1, (B, Sq, Hq, d), case.dtype, case.value_scale)
+    k = _normal_bits(seed, 2, (B, Sk, Hkv, d), case.dtype, case.value_scale)
+    v = _normal_bits(seed, 3, (B, Sk, Hkv, d), case.dtype, case.value_scale)
     if case.poison:
         nan = NAN_BITS[case.dtype]
         for b in range(B):
@@ -137,7 +159,7 @@ def make_prefill_inputs(case: PrefillCase, seed: int = 0) -> PrefillInputs:
 
 
 def make_decode_inputs(case: DecodeCase, seed: int = 0) -> DecodeInputs:
-    rng = np.random.Generator(np.random.PCG64(seed))
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0])))
     B, Hq, Hkv, d = case.batch, case.heads_q, case.heads_kv, case.head_dim
     if case.lengths_fixed is not None:
         lens = np.asarray(case.lengths_fixed, dtype=np.int32)
@@ -145,15 +167,15 @@ def make_decode_inputs(case: DecodeCase, seed: int = 0) -> DecodeInputs:
             raise ValueError("lengths_fixed must have one entry per sequence")
     else:
         lens = rng.integers(case.len_lo, case.len_hi, size=B, endpoint=True).astype(np.int32)
-    q = _normal_bits(rng, (B, 1, Hq, d), case.dtype, 1.0)
+    q = _normal_bits(seed, 1, (B, 1, Hq, d), case.dtype, 1.0)
     if case.layout == "bhsd":
         q = np.ascontiguousarray(q.transpose(0, 2, 1, 3))
     elif case.layout != "bshd":
         raise ValueError(f"unknown layout {case.layout!r}")
     pages = [-(-int(L) // PAGE) for L in lens]
     num_blocks = max(1, sum(pages))
-    kc = _normal_bits(rng, (num_blocks, PAGE, Hkv, d), case.dtype, 1.0)
-    vc = _normal_bits(rng, (num_blocks, PAGE, Hkv, d), case.dtype, 1.0)
+    kc = _normal_bits(seed, 2, (num_blocks, PAGE, Hkv, d), case.dtype, 1.0)
+    vc = _normal_bits(seed, 3, (num_blocks, PAGE, Hkv, d), case.dtype, 1.0)
     perm = rng.permutation(num_blocks).astype(np.int32)
     max_blocks = max(1, max(pages) if pages else 1)
     table = np.zeros((B, max_blocks), dtype=np.int32)

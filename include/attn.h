@@ -1,0 +1,218 @@
+/*
+ * attn.h -- C ABI of the gfx950 (MI355X) tiled attention forward library (libattn.so).
+ *
+ * The library computes scaled-dot-product attention O = softmax(tau * Q K^T) V,
+ * tau = 1/sqrt(d) by default, with the streaming (online) softmax: a running row
+ * maximum m, a running denominator l and an un-normalised output o are carried
+ * across 64-key tiles, each tile rescales the old state by alpha = e^(m_old - m_new),
+ * and O = o / l at the end, so the S_q x S_k score matrix is never stored
+ * (page "gfx942 unified attention, from the math up", sections 1-3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named q, k, v, o, lse, block_table, seqlens_k, partial_*, workspace
+ *    are DEVICE pointers owned by the caller (for instance torch tensors). The
+ *    library allocates no memory and keeps no pointer after a call returns.
+ *  - 16-bit tensors (fp16 / bf16) must be 16-byte aligned and contiguous in the
+ *    stated layout; the head dimension d is the innermost, contiguous axis.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously on it; nothing synchronises inside the library.
+ *  - Every call returns an attn_status_t; no C++ exception crosses the ABI.
+ *    Arguments are validated on the host before any HIP call, so invalid
+ *    arguments are reported even on a machine without a GPU. A non-OK status
+ *    leaves a message readable with attn_last_error() (thread-local).
+ *  - Values stored in the device buffers are not validated (that would need a
+ *    synchronising copy): out-of-range page ids are treated as empty pages and
+ *    key lengths are clamped to their stated host-side bounds, so a bad table
+ *    gives wrong numbers, never an out-of-bounds access.
+ *  - Outputs in fp16 / bf16 are rounded to nearest, ties to even.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+#define ATTN_PAGE_SIZE 64      /* tokens per KV page (block_size); equal to the KV tile width */
+#define ATTN_MAX_SPLITS 64     /* upper bound of num_splits for the split-KV decode */
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,   /* an argument is out of its documented domain */
+  ATTN_ERR_UNSUPPORTED = 2,   /* a valid combination this build does not implement */
+  ATTN_ERR_LAUNCH = 3,        /* the HIP runtime refused the launch */
+  ATTN_ERR_NO_DEVICE = 4      /* no usable HIP device */
+} attn_status_t;
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1, ATTN_F32 = 2 } attn_dtype_t;
+
+/* BSHD = [batch, seq, heads, d]; BHSD = [batch, heads, seq, d]. Both are accepted
+ * as-is, without a transposition (page 7minutos.es / MoonMath, section
+ * "Entendiendo el nucleo"). */
+typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
+
+/*
+ * Prefill (S_q >= 1 queries per sequence).
+ *
+ * Operation: for every sequence b, query head h and query row i (0 <= i < S_q),
+ *   O[b,h,i] = sum_j a_j V_b[j],  a_j = exp(s_j - m) / sum_j' exp(s_j' - m),
+ *   s_j = scale * <Q[b,h,i], K_b[j]>, m = max of the visible s_j,
+ * over the visible keys j (page "gfx942 unified attention, from the math up",
+ * sections 1-2). Key j is visible iff j < L_b and, when causal, j <= i + (L_b - S_q):
+ * the causal mask is aligned to the bottom-right corner (same page, section 4),
+ * and key tiles entirely in a query tile's future are skipped. Query head h reads
+ * KV head floor(h / G), G = num_heads_q / num_heads_kv (GQA; same page, section 5).
+ * A row with no visible key gets O = 0 and lse = -inf.
+ *
+ * Fields:
+ *  q        [B, S_q, Hq, d] (BSHD) or [B, Hq, S_q, d] (BHSD), qkv_dtype.
+ *  k, v     paged (block_table != NULL): caches [num_blocks, 64, Hkv, d]; logical
+ *           key j of sequence b is row j % 64 of page block_table[b*max_blocks_per_seq
+ *           + j / 64] (same page, section 5).
+ *           dense (block_table == NULL): [B, S_k, Hkv, d] (BSHD) or [B, Hkv, S_k, d]
+ *           (BHSD), S_k = seqlen_k, same layout as q.
+ *  o        output, layout of q, o_dtype (F16, BF16 or F32).
+ *  lse      optional (NULL to skip) fp32 [B, Hq, S_q]: natural-log log-sum-exp of the
+ *           scaled visible scores of each row.
+ *  block_table  int32 [B, max_blocks_per_seq], or NULL for dense K/V.
+ *  seqlens_k    int32 [B] per-sequence key lengths L_b (clamped to seqlen_k), or NULL
+ *           for L_b = seqlen_k. Required when block_table != NULL.
+ *  seqlen_k upper bound of the key lengths (dense: the K/V row count).
+ *  head_dim d in {64, 128, 256}. num_heads_q % num_heads_kv == 0, and
+ *           num_heads_q / num_heads_kv <= 128.
+ *  causal   0 or 1. precise: 0 or 1; 1 keeps the probabilities P at ~fp32 precision
+ *           in the P.V product (two fp16/bf16 MFMA terms, hi + lo), for an fp32 O.
+ *  scale    softmax scale; 0 selects 1/sqrt(d).
+ * Errors: INVALID_ARG for null required pointers, misalignment, non-positive
+ * sizes (B or S_q of 0 is a no-op returning OK), d not in {64,128,256}, a head
+ * count that is not a multiple, a paged cache whose table cannot hold seqlen_k
+ * keys (64*max_blocks_per_seq < seqlen_k), bad enum values.
+ */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* block_table;
+  const int32_t* seqlens_k;
+  int32_t batch;
+  int32_t num_heads_q;
+  int32_t num_heads_kv;
+  int32_t seqlen_q;
+  int32_t seqlen_k;
+  int32_t head_dim;
+  int32_t num_blocks;          /* paged: pages in the cache */
+  int32_t max_blocks_per_seq;  /* paged: columns of block_table */
+  int32_t qkv_dtype;           /* attn_dtype_t: F16 or BF16 */
+  int32_t o_dtype;             /* attn_dtype_t: F16, BF16 or F32 */
+  int32_t layout;              /* attn_layout_t */
+  int32_t causal;
+  int32_t precise;
+  float scale;
+} attn_prefill_args_t;
+
+attn_status_t attn_prefill_fwd(const attn_prefill_args_t* args, void* stream);
+
+/*
+ * Split-KV decode (one query per sequence), split kernel + log-sum-exp combine.
+ *
+ * Operation: the attention of attn_prefill_fwd at S_q = 1, non-causal (one query
+ * attends to every key; identical to the bottom-right causal mask at S_q = 1:
+ * page "gfx942 unified attention, from the math up", sections 4 and 8). The keys
+ * of each sequence are split into partitions of P = roundup(ceil(max_seqlen_k /
+ * num_splits), 64) tokens; one workgroup per (sequence, KV head, partition) handles
+ * the G query heads of the group and writes a partial (O_s normalised, lse_s) to the
+ * workspace; the combine then merges them (see attn_splitkv_combine). Both kernels
+ * run on `stream` in order.
+ *
+ * Fields:
+ *  q          [B, Hq, d] (the BSHD and BHSD layouts coincide at S_q = 1), qkv_dtype.
+ *  k_cache, v_cache  [num_blocks, 64, Hkv, d], qkv_dtype.
+ *  block_table int32 [B, max_blocks_per_seq]; seqlens_k int32 [B] (clamped to
+ *             max_seqlen_k, which must be <= 64*max_blocks_per_seq).
+ *  o          [B, Hq, d], o_dtype. lse: optional fp32 [B, Hq].
+ *  workspace  device buffer of at least attn_decode_workspace_bytes(B, Hq,
+ *             num_splits, d) bytes, 256-byte aligned; caller-owned scratch, reused
+ *             freely between calls on the same stream.
+ *  num_splits 1..ATTN_MAX_SPLITS. num_heads_q / num_heads_kv <= 16.
+ * Errors: as for prefill, plus INVALID_ARG for a too-small or misaligned workspace.
+ */
+typedef struct {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seqlens_k;
+  void* o;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t batch;
+  int32_t num_heads_q;
+  int32_t num_heads_kv;
+  int32_t head_dim;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_seqlen_k;
+  int32_t num_splits;
+  int32_t qkv_dtype;
+  int32_t o_dtype;
+  float scale;
+} attn_decode_args_t;
+
+attn_status_t attn_decode_fwd(const attn_decode_args_t* args, void* stream);
+
+/* Bytes of decode workspace: fp32 partial outputs [B, Hq, num_splits, d] followed
+ * (at a 256-byte aligned offset) by fp32 partial lse [B, Hq, num_splits]. Returns 0
+ * for invalid sizes. */
+size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_heads_q, int32_t num_splits,
+                                   int32_t head_dim);
+
+/*
+ * Log-sum-exp combine of split partial results (page "gfx942 unified attention,
+ * from the math up", section 8: partial softmax-weighted outputs of the KV splits
+ * are combined). For each (b, h):
+ *   M = max_s lse_s,  w_s = exp(lse_s - M),  O = sum_s w_s O_s / sum_s w_s,
+ *   lse = M + ln(sum_s w_s).
+ * A split with lse_s = -inf (no key) has weight 0 and its O_s is not read; if every
+ * split is empty, O = 0 and lse = -inf.
+ *
+ * Fields: partial_o fp32 [B, H, num_splits, d] (each O_s already normalised);
+ * partial_lse fp32 [B, H, num_splits] (natural log); o [B, H, d] in o_dtype;
+ * lse optional fp32 [B, H]; num_splits 1..ATTN_MAX_SPLITS; d in {64, 128, 256}.
+ * Errors: INVALID_ARG for null pointers, sizes or dtype out of range.
+ */
+typedef struct {
+  const float* partial_o;
+  const float* partial_lse;
+  void* o;
+  float* lse;
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_splits;
+  int32_t head_dim;
+  int32_t o_dtype;
+} attn_combine_args_t;
+
+attn_status_t attn_splitkv_combine(const attn_combine_args_t* args, void* stream);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int32_t attn_abi_version(void);
+
+/* Number of visible HIP devices (0 when none or when the runtime is unavailable). */
+int32_t attn_device_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU parity tests: device copies of the seeded inputs,
+calls through the C ABI (via the binding), and oracle evaluations."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from attn_workloads import bits_to_f64
+
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+TOL = {"f16": 2e-2, "bf16": 4e-2}
+TOL_PRECISE = 1e-4
+
+
+def say(msg: str):
+    """Name the case before any GPU work, flushed, so a failing run says where it was."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH_DT[dtype])
+    return t.cuda()
+
+
+def dev_i32(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def tolerance(case) -> float:
+    return TOL_PRECISE if getattr(case, "precise", False) else TOL[case.dtype]
+
+
+def gpu_prefill(inp, *, with_lse=False, out_dtype=None):
+    """Run attn_prefill_fwd on the seeded inputs; returns (O, lse) as float64 numpy."""
+    from attention_forward_tiled_amd import attn_prefill_fwd
+    c = inp.case
+    q, k, v = dev(inp.q, c.dtype), dev(inp.k, c.dtype), dev(inp.v, c.dtype)
+    bt = dev_i32(inp.block_table) if inp.block_table is not None else None
+    sl = dev_i32(inp.seqlens_k) if (inp.block_table is not None or c.seqlens_k is not None) else None
+    odt = TORCH_DT[out_dtype or c.o_dtype]
+    lse = None
+    if with_lse:
+        lse = torch.full((c.batch, c.heads_q, c.seqlen_q), float("nan"), dtype=torch.float32, device="cuda")
+    o = attn_prefill_fwd(q, k, v, causal=c.causal, block_table=bt, seqlens_k=sl,
+                         seqlen_k=c.seqlen_k, layout=c.layout, out_dtype=odt, lse=lse,
+                         precise=c.precise)
+    torch.cuda.synchronize()
+    return to_f64(o), (to_f64(lse) if lse is not None else None)
+
+
+def oracle_prefill(inp, q_index=None):
+    c = inp.case
+    q = bits_to_f64(inp.q, c.dtype)
+    k = bits_to_f64(inp.k, c.dtype)
+    v = bits_to_f64(inp.v, c.dtype)
+    return oracle.attention(q, k, v, causal=c.causal, layout=c.layout, block_table=inp.block_table,
+                            seqlens_k=inp.seqlens_k, q_index=q_index)
+
+
+def max_abs_err(a: np.ndarray, b: np.ndarray) -> float:
+    if a.shape != b.shape:
+        raise AssertionError(f"shape mismatch {a.shape} vs {b.shape}")
+    if not np.isfinite(a).all():
+        return float("inf")
+    return float(np.abs(a - b).max()) if a.size else 0.0

@@ -1,0 +1,152 @@
+"""The C ABI without a GPU: every declared symbol is exported, and invalid
+arguments are rejected on the host with the documented status and a message."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_forward_tiled_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[a-z_0-9]+\s*\*?\s+)+(attn_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.attn_abi_version() == _lib.ATTN_ABI_VERSION
+
+
+def test_header_constants_match_binding():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    assert f"#define ATTN_PAGE_SIZE {_lib.ATTN_PAGE_SIZE} " in text
+    assert f"#define ATTN_MAX_SPLITS {_lib.ATTN_MAX_SPLITS} " in text
+    assert f"#define ATTN_ABI_VERSION {_lib.ATTN_ABI_VERSION}" in text
+
+
+def test_struct_sizes():
+    # the ctypes mirrors must have the C layout (all fields naturally aligned, no padding holes)
+    assert ctypes.sizeof(_lib.PrefillArgs) == 7 * 8 + 14 * 4
+    assert ctypes.sizeof(_lib.DecodeArgs) == 8 * 8 + 8 + 11 * 4 + 4
+    assert ctypes.sizeof(_lib.CombineArgs) == 4 * 8 + 5 * 4 + 4
+
+
+FAKE = 0x1000  # aligned non-null pointer value; never dereferenced (validation fails first)
+
+
+def prefill_args(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, block_table=FAKE, seqlens_k=FAKE,
+             batch=1, num_heads_q=4, num_heads_kv=2, seqlen_q=128, seqlen_k=128, head_dim=128,
+             num_blocks=2, max_blocks_per_seq=2, qkv_dtype=_lib.ATTN_F16, o_dtype=_lib.ATTN_F16,
+             layout=_lib.ATTN_BSHD, causal=1, precise=0, scale=0.0)
+    a.update(kw)
+    return _lib.PrefillArgs(**a)
+
+
+def decode_args(**kw):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, block_table=FAKE, seqlens_k=FAKE, o=FAKE, lse=None,
+             workspace=FAKE, workspace_bytes=1 << 30, batch=2, num_heads_q=8, num_heads_kv=2,
+             head_dim=128, num_blocks=10, max_blocks_per_seq=5, max_seqlen_k=300, num_splits=4,
+             qkv_dtype=_lib.ATTN_BF16, o_dtype=_lib.ATTN_BF16, scale=0.0)
+    a.update(kw)
+    return _lib.DecodeArgs(**a)
+
+
+def combine_args(**kw):
+    a = dict(partial_o=FAKE, partial_lse=FAKE, o=FAKE, lse=None, batch=2, num_heads=4, num_splits=8,
+             head_dim=128, o_dtype=_lib.ATTN_F32)
+    a.update(kw)
+    return _lib.CombineArgs(**a)
+
+
+BAD_PREFILL = [
+    (dict(head_dim=96), _lib.ATTN_ERR_INVALID_ARG, "head_dim"),
+    (dict(num_heads_q=5, num_heads_kv=2), _lib.ATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(num_heads_kv=0), _lib.ATTN_ERR_INVALID_ARG, "positive"),
+    (dict(qkv_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_INVALID_ARG, "qkv_dtype"),
+    (dict(o_dtype=7), _lib.ATTN_ERR_INVALID_ARG, "o_dtype"),
+    (dict(layout=2), _lib.ATTN_ERR_INVALID_ARG, "layout"),
+    (dict(causal=2), _lib.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(q=None), _lib.ATTN_ERR_INVALID_ARG, "non-NULL"),
+    (dict(o=FAKE + 2), _lib.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(seqlens_k=None), _lib.ATTN_ERR_INVALID_ARG, "seqlens_k"),
+    (dict(max_blocks_per_seq=1), _lib.ATTN_ERR_INVALID_ARG, "fewer than seqlen_k"),
+    (dict(scale=float("nan")), _lib.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(num_heads_q=258, num_heads_kv=2), _lib.ATTN_ERR_UNSUPPORTED, "GQA"),
+    (dict(batch=-1), _lib.ATTN_ERR_INVALID_ARG, "batch"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_PREFILL, ids=lambda x: str(x)[:40])
+def test_prefill_rejects(lib, kw, status, msg):
+    st = lib.attn_prefill_fwd(ctypes.byref(prefill_args(**kw)), None)
+    assert st == status
+    assert msg in _lib.last_error()
+
+
+def test_null_args_pointer(lib):
+    assert lib.attn_prefill_fwd(None, None) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_decode_fwd(None, None) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_splitkv_combine(None, None) == _lib.ATTN_ERR_INVALID_ARG
+
+
+def test_prefill_empty_is_noop(lib):
+    assert lib.attn_prefill_fwd(ctypes.byref(prefill_args(batch=0, q=None)), None) == _lib.ATTN_OK
+    assert lib.attn_prefill_fwd(ctypes.byref(prefill_args(seqlen_q=0, q=None)), None) == _lib.ATTN_OK
+    assert _lib.last_error() == ""
+
+
+BAD_DECODE = [
+    (dict(num_splits=0), _lib.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(num_splits=65), _lib.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(num_heads_q=64, num_heads_kv=2), _lib.ATTN_ERR_UNSUPPORTED, "GQA"),
+    (dict(workspace_bytes=16), _lib.ATTN_ERR_INVALID_ARG, "workspace"),
+    (dict(workspace=FAKE + 16), _lib.ATTN_ERR_INVALID_ARG, "256-byte"),
+    (dict(max_seqlen_k=321), _lib.ATTN_ERR_INVALID_ARG, "fewer than max_seqlen_k"),
+    (dict(block_table=None), _lib.ATTN_ERR_INVALID_ARG, "non-NULL"),
+    (dict(head_dim=32), _lib.ATTN_ERR_INVALID_ARG, "head_dim"),
+    (dict(qkv_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_INVALID_ARG, "qkv_dtype"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_DECODE, ids=lambda x: str(x)[:40])
+def test_decode_rejects(lib, kw, status, msg):
+    st = lib.attn_decode_fwd(ctypes.byref(decode_args(**kw)), None)
+    assert st == status
+    assert msg in _lib.last_error()
+
+
+@pytest.mark.parametrize("kw,msg", [(dict(num_splits=0), "num_splits"), (dict(head_dim=100), "head_dim"),
+                                    (dict(o_dtype=3), "o_dtype"), (dict(partial_o=None), "non-NULL")])
+def test_combine_rejects(lib, kw, msg):
+    assert lib.attn_splitkv_combine(ctypes.byref(combine_args(**kw)), None) == _lib.ATTN_ERR_INVALID_ARG
+    assert msg in _lib.last_error()
+
+
+def test_workspace_bytes(lib):
+    n = lib.attn_decode_workspace_bytes(32, 32, 16, 128)
+    assert n >= 32 * 32 * 16 * 129 * 4 and n % 256 == 0
+    assert lib.attn_decode_workspace_bytes(1, 1, 65, 128) == 0
+    assert lib.attn_decode_workspace_bytes(1, 1, 1, 100) == 0
+
+
+@pytest.mark.skipif(_lib.load().attn_device_count() > 0, reason="a GPU is present; fake pointers must not launch")
+def test_valid_call_without_device_reports_no_device(lib):
+    assert lib.attn_prefill_fwd(ctypes.byref(prefill_args()), None) == _lib.ATTN_ERR_NO_DEVICE
+    assert lib.attn_decode_fwd(ctypes.byref(decode_args()), None) == _lib.ATTN_ERR_NO_DEVICE
+    assert lib.attn_splitkv_combine(ctypes.byref(combine_args()), None) == _lib.ATTN_ERR_NO_DEVICE

@@ -1,0 +1,135 @@
+"""GPU parity of the split-KV decode (attn_decode_fwd) and the standalone
+log-sum-exp combine (attn_splitkv_combine) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attn_workloads import CONFIGS, DecodeCase, bits_to_f64, make_decode_inputs
+from gpu_util import TOL, dev, dev_i32, max_abs_err, say, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def gpu_decode(inp, num_splits, out_dtype=None, with_lse=False):
+    from attention_forward_tiled_amd import attn_decode_fwd
+    c = inp.case
+    lse = torch.full((c.batch, c.heads_q), float("nan"), device="cuda") if with_lse else None
+    o = attn_decode_fwd(dev(inp.q, c.dtype), dev(inp.k_cache, c.dtype), dev(inp.v_cache, c.dtype),
+                        dev_i32(inp.block_table), dev_i32(inp.seqlens_k),
+                        max_seqlen_k=inp.max_seqlen_k, num_splits=num_splits,
+                        out_dtype=out_dtype, lse=lse)
+    torch.cuda.synchronize()
+    return to_f64(o), (to_f64(lse) if with_lse else None)
+
+
+def oracle_decode(inp, seqs=None):
+    """fp64 oracle on the chosen sequences only (their pages copied out of the pool)."""
+    c = inp.case
+    seqs = list(range(c.batch)) if seqs is None else list(seqs)
+    tables, pages = [], []
+    for b in seqs:
+        n = -(-int(inp.seqlens_k[b]) // 64)
+        tables.append(list(range(len(pages), len(pages) + n)))
+        pages.extend(int(x) for x in inp.block_table[b, :n])
+    width = max(1, max(len(t) for t in tables))
+    table = np.zeros((len(seqs), width), dtype=np.int64)
+    for i, t in enumerate(tables):
+        table[i, :len(t)] = t
+    pages = pages or [0]
+    k = bits_to_f64(inp.k_cache[pages], c.dtype)
+    v = bits_to_f64(inp.v_cache[pages], c.dtype)
+    q = bits_to_f64(inp.q[seqs], c.dtype)                      # [n, 1, Hq, d]
+    O, lse = oracle.attention(q, k, v, causal=False, block_table=table,
+                              seqlens_k=inp.seqlens_k[seqs])
+    return O[:, 0], lse[:, :, 0]
+
+
+SMALL = [
+    (DecodeCase("bf16_g4_d128", 5, 8, 2, 128, "bf16", lengths_fixed=(1, 63, 64, 65, 1000)), (1, 3, 16)),
+    (DecodeCase("f16_g1_d128", 4, 4, 4, 128, "f16", lengths_fixed=(700, 129, 4096, 5)), (1, 7)),
+    (DecodeCase("bf16_g8_d64", 3, 16, 2, 64, "bf16", lengths_fixed=(333, 64, 2000)), (2, 16)),
+    (DecodeCase("f16_g16_d128", 2, 32, 2, 128, "f16", lengths_fixed=(1500, 257)), (4,)),
+    (DecodeCase("bf16_g2_d256", 3, 4, 2, 256, "bf16", lengths_fixed=(900, 1, 190)), (1, 5)),
+    (DecodeCase("f16_g3_d128", 2, 6, 2, 128, "f16", lengths_fixed=(640, 641)), (10,)),
+]
+
+
+@pytest.mark.parametrize("case,splits", SMALL, ids=lambda x: getattr(x, "name", str(x)))
+def test_decode_small(case, splits):
+    inp = make_decode_inputs(case, seed=5)
+    Oref, lref = oracle_decode(inp)
+    for s in splits:
+        say(f"decode parity {case} num_splits={s}")
+        O, lse = gpu_decode(inp, s, with_lse=True)
+        err = max_abs_err(O, Oref)
+        say(f"  max abs err {err:.3e}")
+        assert err <= TOL[case.dtype]
+        assert np.abs(lse - lref).max() <= 1e-3
+
+
+def test_decode_split_count_invariance():
+    case = DecodeCase("inv", 3, 8, 2, 128, "bf16", lengths_fixed=(3000, 64, 1777))
+    inp = make_decode_inputs(case, seed=6)
+    outs = []
+    for s in (1, 2, 16, 64):
+        say(f"decode split invariance num_splits={s}")
+        outs.append(gpu_decode(inp, s, out_dtype=torch.float32)[0])
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 2e-2
+
+
+def test_named_decode_full():
+    case = CONFIGS["splitkv_decode_bf16_64k"]
+    say(f"decode parity (full size, sampled sequences) {case.name}")
+    inp = make_decode_inputs(case, seed=0)
+    O, _ = gpu_decode(inp, case.num_splits)
+    lens = inp.seqlens_k
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, case.batch - 1})
+    Oref, _ = oracle_decode(inp, pick)
+    err = max_abs_err(O[pick], Oref)
+    say(f"  max abs err {err:.3e} over sequences {pick} (lengths {lens[pick].tolist()})")
+    assert err <= TOL[case.dtype]
+    assert np.isfinite(O).all()
+
+
+def test_decode_deterministic():
+    case = DecodeCase("det", 4, 32, 8, 128, "bf16", lengths_fixed=(5000, 20000, 64, 1))
+    inp = make_decode_inputs(case, seed=7)
+    say("decode determinism")
+    a, _ = gpu_decode(inp, 16)
+    b, _ = gpu_decode(inp, 16)
+    np.testing.assert_array_equal(a, b)
+
+
+def _partials(seed, B=3, H=5, S=7, d=128):
+    rng = np.random.default_rng(seed)
+    po = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    pl = (rng.standard_normal((B, H, S)) * 20).astype(np.float32)
+    pl[0, 0, :] = -np.inf                 # every split empty
+    pl[0, 1, 1:] = -np.inf                # a single non-empty split
+    pl[1, 2, ::2] = -np.inf
+    pl[2, 3, 3] = 80.0                    # one split dominates
+    po[np.isneginf(pl)] = np.nan          # an empty split's O_s must never be read
+    return po, pl
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
+def test_combine_against_formula(d, odt):
+    from attention_forward_tiled_amd import attn_splitkv_combine
+    say(f"combine parity d={d} out={odt}")
+    po, pl = _partials(d, d=d)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[odt]
+    lse = torch.empty(pl.shape[:2], device="cuda")
+    o = attn_splitkv_combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                             out_dtype=tdt, lse=lse)
+    torch.cuda.synchronize()
+    Oref, lref = oracle.lse_combine(po.astype(np.float64), pl.astype(np.float64))
+    tol = {"f32": 1e-5, "bf16": 4e-2, "f16": 2e-2}[odt]
+    assert max_abs_err(to_f64(o), Oref) <= tol
+    L = to_f64(lse)
+    assert np.isneginf(L[0, 0]) and np.isneginf(lref[0, 0])
+    fin = np.isfinite(lref)
+    assert np.abs(L[fin] - lref[fin]).max() <= 1e-4

@@ -1,0 +1,107 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Element-by-element max-abs error on the same seeded inputs, with the tolerances
+fp16 2e-2, bf16 4e-2, and 1e-4 for the fp32-accumulated precise mode. Small
+cases span several 64-key tiles and a ragged tail; the named workloads run at
+full size in the launch configuration the benchmark times, the largest ones
+checked on sampled outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from attn_workloads import CONFIGS, PrefillCase, make_prefill_inputs
+from gpu_util import gpu_prefill, max_abs_err, oracle_prefill, say, tolerance
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+P = PrefillCase
+SMALL = [
+    P("f16_d64_causal_paged", 2, 4, 2, 200, 200, 64, "f16", True, "paged"),
+    P("bf16_d64_causal_paged_chunked", 2, 4, 2, 70, 190, 64, "bf16", True, "paged"),
+    P("f16_d128_causal_paged", 2, 8, 2, 130, 300, 128, "f16", True, "paged"),
+    P("bf16_d128_causal_paged", 1, 8, 8, 257, 257, 128, "bf16", True, "paged"),
+    P("f16_d256_causal_paged", 1, 2, 1, 150, 150, 256, "f16", True, "paged"),
+    P("bf16_d256_noncausal_dense", 2, 2, 2, 70, 133, 256, "bf16", False, "dense"),
+    P("bf16_d128_noncausal_dense_bhsd", 2, 4, 4, 100, 257, 128, "bf16", False, "dense", layout="bhsd"),
+    P("f16_d128_noncausal_dense_cross", 1, 4, 2, 333, 65, 128, "f16", False, "dense"),
+    P("f16_d64_causal_dense_bhsd", 2, 4, 1, 129, 129, 64, "f16", True, "dense", layout="bhsd"),
+    P("bf16_sq1_noncausal_paged", 3, 8, 2, 1, 500, 128, "bf16", False, "paged"),
+    P("f16_sq1_causal_paged", 3, 8, 2, 1, 77, 128, "f16", True, "paged"),
+    P("f16_gqa3", 1, 6, 2, 100, 100, 128, "f16", True, "paged"),
+    P("bf16_gqa8", 1, 16, 2, 90, 200, 128, "bf16", True, "paged"),
+    P("bf16_gqa16", 1, 32, 2, 40, 128, 64, "bf16", True, "paged"),
+    P("f16_ragged_lengths", 3, 4, 2, 100, 300, 128, "f16", True, "paged", seqlens_k=(300, 100, 37)),
+    P("bf16_ragged_dense", 3, 4, 4, 64, 200, 128, "bf16", False, "dense", seqlens_k=(200, 1, 130)),
+    P("f16_precise_d128", 1, 2, 1, 150, 150, 128, "f16", True, "paged", out_dtype="f32", precise=True),
+    P("bf16_f32_out", 1, 2, 2, 96, 96, 128, "bf16", True, "paged", out_dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c.name)
+def test_prefill_small(case):
+    say(f"prefill parity {case}")
+    inp = make_prefill_inputs(case, seed=1)
+    O, lse = gpu_prefill(inp, with_lse=True)
+    Oref, lref = oracle_prefill(inp)
+    err = max_abs_err(O, Oref)
+    say(f"  max abs err {err:.3e} (tol {tolerance(case)})")
+    assert err <= tolerance(case)
+    fin = np.isfinite(lref)
+    assert (np.isneginf(lse) == ~fin).all()
+    assert np.abs(lse[fin] - lref[fin]).max() <= 1e-3
+
+
+def test_prefill_rows_without_keys_are_zero():
+    # causal with a key length shorter than S_q: the first rows see no key at all
+    case = P("empty_rows", 1, 2, 1, 100, 100, 128, "f16", True, "paged", seqlens_k=(40,))
+    say(f"prefill parity {case}")
+    inp = make_prefill_inputs(case, seed=2)
+    O, lse = gpu_prefill(inp, with_lse=True)
+    Oref, lref = oracle_prefill(inp)
+    assert (O[0, :60] == 0).all() and np.isneginf(lse[0, :, :60]).all()
+    assert max_abs_err(O, Oref) <= tolerance(case)
+
+
+def test_paged_equals_dense_bitwise():
+    base = P("pd", 2, 8, 2, 200, 200, 128, "bf16", True, "paged")
+    say(f"paged vs dense {base}")
+    a, _ = gpu_prefill(make_prefill_inputs(base, seed=3))
+    b, _ = gpu_prefill(make_prefill_inputs(base.with_(kv="dense"), seed=3))
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["tiny_causal_f16_d64", "gqa_causal_paged_f16_s2048",
+                                  "chunked_prefill_bf16_512x4096"])
+def test_named_prefill_full(name):
+    case = CONFIGS[name]
+    say(f"prefill parity (full output) {name}")
+    inp = make_prefill_inputs(case, seed=0)
+    O, _ = gpu_prefill(inp)
+    Oref, _ = oracle_prefill(inp)
+    err = max_abs_err(O, Oref)
+    say(f"  max abs err {err:.3e} (tol {tolerance(case)})")
+    assert err <= tolerance(case)
+
+
+def test_named_long_noncausal_sampled():
+    case = CONFIGS["long_noncausal_bf16_s16384"]
+    say(f"prefill parity (sampled rows) {case.name}")
+    inp = make_prefill_inputs(case, seed=0)
+    O, _ = gpu_prefill(inp)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, case.seqlen_q - 1],
+                                     np.random.default_rng(0).choice(case.seqlen_q, 25, replace=False)]))
+    Oref, _ = oracle_prefill(inp, q_index=rows)
+    err = max_abs_err(O[:, rows], Oref)
+    say(f"  max abs err {err:.3e} over {rows.size} rows x all (b, h)")
+    assert err <= tolerance(case)
+
+
+def test_prefill_deterministic():
+    case = CONFIGS["gqa_causal_paged_f16_s2048"]
+    say(f"determinism {case.name}")
+    inp = make_prefill_inputs(case, seed=4)
+    a, _ = gpu_prefill(inp)
+    b, _ = gpu_prefill(inp)
+    np.testing.assert_array_equal(a, b)
