@@ -35,6 +35,32 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr float kLazy = 8.0f;          // log2-domain slack before the reference max moves
+constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched
+
+
+// 16 bytes of zeros in global memory: the source of every LDS row past a key length.
+__device__ __align__(16) const uint16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// Wave-uniform byte address of a shared-memory location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)(p));
+}
+
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane l's 16 bytes land
+// at LDS byte lds + 16 * l. Issued from inline asm so that the compiler does not fence LDS
+// reads of the other stage on it; completion is awaited explicitly (vmcnt) before the
+// barrier that publishes the stage.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// Read-only device int through the constant address space, so it becomes a scalar load.
+__device__ __forceinline__ int scalar_load(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(p);
+}
 
 // 16-byte chunk swizzle: spreads the 16 rows read by one 16-lane group over 256 bytes
 // of banks. Rows of 128 bytes (d = 64) pair up before the XOR so that two consecutive
@@ -51,13 +77,14 @@ __device__ __forceinline__ int lds_off(int row, int col) {  // col in elements, 
 }
 
 template <int D, typename T, bool PRECISE>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void prefill_kernel(const PrefillParams p) {
   constexpr int KS = D / 32;            // k-steps of the S^T product
   constexpr int DB = D / 16;            // 16-wide d blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int LPT = CPR * kPage / kThreads;   // chunks per thread per tile (K and V each)
+  constexpr int RPI = 512 / D;          // rows covered by one 1 KiB wave-wide LDS load
+  constexpr int NIW = kPage / RPI / kWaves;   // such loads per wave per tile (K and V each)
   constexpr int TILE = kPage * D;       // elements per K (or V) tile
-  extern __shared__ __align__(16) uint16_t smem[];   // [2 buffers][K, V][TILE]
+  extern __shared__ __align__(16) uint16_t smem[];   // [2 stages][K, V][TILE]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -68,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
   if (p.seqlens_k) L = min(max(p.seqlens_k[b], 0), p.seqlen_k);
   const int q0 = qblk * p.bq;
   const int off = L - p.seqlen_q;       // bottom-right alignment of the causal mask
+  const float c = p.scale_log2;
 
   // ---- this lane's two query rows (one per 16-row block) and their Q fragments
   int rpos[2], rh[2];
@@ -90,58 +118,52 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
   const int kv_end = p.causal ? min(L, pmax + off + 1) : L;
   const int n_tiles = kv_end > 0 ? (kv_end + kPage - 1) / kPage : 0;
 
-  // ---- K/V tile loader: thread-owned 16-byte chunks, zero past the key length
-  u32x4 kr[LPT], vr[LPT];
-  auto load_tile = [&](int j) {
+  // ---- K/V tile loads straight into LDS (global_load_lds_dwordx4). One wave-wide load
+  // fills 1 KiB = RPI rows; lane l lands at byte 16*l of it, so the XOR swizzle is applied
+  // by choosing which 16-byte chunk of its row each lane fetches. Rows past the key length
+  // (or of an invalid page) fetch a 16-byte block of zeros instead.
+  const int r_in = lane / CPR, pc = lane % CPR;
+  auto issue_tile = [&](int j, int stage) {
     int64_t base;
+    int64_t rs;
     bool page_ok = true;
     if (p.block_table) {
-      const int pg = p.block_table[(int64_t)b * p.max_blocks + j];
+      const int pg = scalar_load(p.block_table + (int64_t)b * p.max_blocks + j);
       page_ok = pg >= 0 && pg < p.num_blocks;
       base = (int64_t)(page_ok ? pg : 0) * kPage * p.hkv * D + (int64_t)kvh * D;
+      rs = (int64_t)p.hkv * D;
     } else {
       base = b * p.kv_sb + kvh * p.kv_sh + (int64_t)j * kPage * p.kv_ss;
+      rs = p.kv_ss;
     }
-    const int64_t rs = p.block_table ? (int64_t)p.hkv * D : p.kv_ss;
+    const uint32_t ks = lds_addr(smem + stage * 2 * TILE);
+    const uint32_t vs = ks + TILE * sizeof(uint16_t);
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + i * kThreads;
-      const int t = c / CPR, ch = c % CPR;
-      const bool ok = page_ok && (j * kPage + t < L);
-      const int64_t e = base + t * rs + ch * 8;
-      kr[i] = ok ? ldg16(p.k + e) : u32x4{0, 0, 0, 0};
-      vr[i] = ok ? ldg16(p.v + e) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * 2 * TILE;
-    uint16_t* vs = ks + TILE;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + i * kThreads;
-      const int t = c / CPR, ch = c % CPR;
-      const int o = t * D + ((ch ^ swz<D>(t)) << 3);
-      *reinterpret_cast<u32x4*>(ks + o) = kr[i];
-      *reinterpret_cast<u32x4*>(vs + o) = vr[i];
+    for (int k = 0; k < NIW; ++k) {
+      const int i = wave * NIW + k;
+      const int r = i * RPI + r_in;
+      const bool ok = page_ok && (j * kPage + r < L);
+      const int64_t e = base + r * rs + ((pc ^ swz<D>(r)) << 3);
+      dma16(ok ? p.k + e : kZeroChunk, ks + i * 1024);
+      dma16(ok ? p.v + e : kZeroChunk, vs + i * 1024);
     }
   };
 
-  float m[2] = {-INFINITY, -INFINITY};
+  float mref[2] = {-INFINITY, -INFINITY};   // reference max (log2 domain) of o and l
   float lsum[2] = {0.f, 0.f};
   float4v acc[DB][2];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = float4v{0, 0, 0, 0};
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  if (n_tiles > 0) issue_tile(0, 0);
 
   for (int j = 0; j < n_tiles; ++j) {
+    // tile j has landed (own loads), every wave is past tile j-1: publish and recycle
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (j + 1 < n_tiles) issue_tile(j + 1, (j + 1) & 1);
     const uint16_t* ks = smem + (j & 1) * 2 * TILE;
     const uint16_t* vs = ks + TILE;
-    if (j + 1 < n_tiles) load_tile(j + 1);
 
     // ---- S^T = K Q^T for 64 keys x 32 queries
     float4v s[4][2];
@@ -157,45 +179,60 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
       }
     }
 
-    // ---- online softmax update (base-2 domain); masks only on tiles that need them
+    // ---- online softmax (base-2 domain) with a lazily moved reference maximum: o and l
+    // are kept relative to mref, which only moves (rescaling o and l by 2^(old - new)) when
+    // a row's maximum exceeds it by more than kLazy; every p stays <= 2^kLazy.
     const bool need_mask = (j * kPage + kPage - 1 >= L) ||
                            (p.causal && j * kPage + kPage - 1 > q0 + off);
-    u32x4 pf[2][2];
-    u32x4 pl[2][2];
+    float mt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float x[4][4];
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = s[kb][qb][i] * p.scale_log2;
+          float v = s[kb][qb][i];
           if (need_mask) {
             const int key = j * kPage + kb * 16 + lg * 4 + i;
             const bool vis = key < L && (!p.causal || key <= rpos[qb] + off);
             v = vis ? v : -INFINITY;
+            s[kb][qb][i] = v;
           }
-          x[kb][i] = v;
           mx = fmaxf(mx, v);
         }
       mx = wave_max_xor(mx, 16);
       mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m[qb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m[qb] - m_use);
-      m[qb] = m_new;
+      mt[qb] = mx * c;
+    }
+    const bool up0 = mt[0] > mref[0] + kLazy, up1 = mt[1] > mref[1] + kLazy;
+    if (__builtin_amdgcn_ballot_w64(up0 || up1) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bool up = qb ? up1 : up0;
+        const float nref = up ? mt[qb] : mref[qb];
+        const float alpha = up ? fast_exp2(mref[qb] - nref) : 1.f;
+        mref[qb] = nref;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+      }
+    }
+    u32x4 pf[2][2];
+    u32x4 pl[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mneg = mref[qb] == -INFINITY ? 0.f : -mref[qb];
+      float x[4][4];
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[kb][i] = fast_exp2(x[kb][i] - m_use);
+          x[kb][i] = fast_exp2(__builtin_fmaf(s[kb][qb][i], c, mneg));
           ps += x[kb][i];
         }
-      lsum[qb] = lsum[qb] * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+      lsum[qb] += ps;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const float* a0 = x[2 * s2];
@@ -233,12 +270,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
         }
       }
     }
-
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
-    __syncthreads();
   }
 
-  // ---- epilogue: O = o / l, lse = ln 2 * (m + log2 l)
+  // ---- epilogue: O = o / l, lse = ln 2 * (mref + log2 l)
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float l = wave_sum_xor(lsum[qb], 16);
@@ -262,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     }
     if (p.lse && lg == 0)
       p.lse[((int64_t)b * p.hq + rh[qb]) * p.seqlen_q + rpos[qb]] =
-          l > 0.f ? (m[qb] + __log2f(l)) * kLn2 : -INFINITY;
+          l > 0.f ? (mref[qb] + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
