@@ -25,6 +25,10 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short2v __attribute__((ext_vector_type(2)));
 
 constexpr int kPage = 64;          // tokens per KV page == KV tile width T
 constexpr float kLog2e = 1.4426950408889634f;
@@ -48,6 +52,14 @@ template <> struct Op<F16> {
   static __device__ __forceinline__ float to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
   }
+  // Two floats -> two fp16 (round to nearest even) in one dword, lo first (v_cvt_pk_f16_f32).
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, half2v));
+  }
+  // acc + lo + hi of a packed pair, accumulated in fp32 (v_dot2c_f32_f16 against (1, 1)).
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pair), half2v{1, 1}, acc, false);
+  }
 };
 template <> struct Op<BF16> {
   typedef bf16x8 vec;
@@ -62,6 +74,15 @@ template <> struct Op<BF16> {
   static __device__ __forceinline__ float to_float(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
   }
+  // Two floats -> two bf16 (round to nearest even) in one dword, lo first (v_cvt_pk_bf16_f32).
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2));
+  }
+  // acc + lo + hi of a packed pair, accumulated in fp32 (v_dot2c_f32_bf16 against (1, 1)).
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2v, pair),
+                                          short2v{0x3F80, 0x3F80}, acc, false);
+  }
 };
 
 template <typename T>
@@ -69,10 +90,10 @@ __device__ __forceinline__ typename Op<T>::vec as_op(const u32x4& r) {
   return __builtin_bit_cast(typename Op<T>::vec, r);
 }
 
-// Pack two floats into one dword of two 16-bit values (lo first).
+// Pack two floats into one dword of two 16-bit values (lo first), round to nearest even.
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)Op<T>::from_float(lo) | ((uint32_t)Op<T>::from_float(hi) << 16);
+  return Op<T>::pack(lo, hi);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -83,6 +104,10 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 __device__ __forceinline__ float wave_sum_xor(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave).
+__device__ __forceinline__ float rows4_max(float x) { return wave_max_xor(wave_max_xor(x, 16), 32); }
+__device__ __forceinline__ float rows4_sum(float x) { return wave_sum_xor(wave_sum_xor(x, 16), 32); }
 
 // LDS transpose read of four 16-bit values (see the header comment).
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {

@@ -16,6 +16,17 @@ from gpu_util import gpu_prefill, max_abs_err, oracle_prefill, say, tolerance
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
+
+
+def lse_tolerance(case):
+    """The row sums l are taken from P after its round-to-nearest-even to the input dtype
+    (the values the P.V product consumes), so ln l carries up to one unit roundoff of that
+    type: 2^-8 for bf16, 2^-11 for fp16; the precise mode sums fp32 P."""
+    if case.precise:
+        return 1e-4
+    return {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}[case.dtype] + 1e-4
+
+
 P = PrefillCase
 SMALL = [
     P("f16_d64_causal_paged", 2, 4, 2, 200, 200, 64, "f16", True, "paged"),
@@ -50,7 +61,7 @@ def test_prefill_small(case):
     assert err <= tolerance(case)
     fin = np.isfinite(lref)
     assert (np.isneginf(lse) == ~fin).all()
-    assert np.abs(lse[fin] - lref[fin]).max() <= 1e-3
+    assert np.abs(lse[fin] - lref[fin]).max() <= lse_tolerance(case)
 
 
 def test_prefill_rows_without_keys_are_zero():
