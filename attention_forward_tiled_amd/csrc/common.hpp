@@ -6,6 +6,10 @@
 //     A: lane l holds A[l % 16][8*(l/16) + j], j = 0..7   (8 halves per lane)
 //     B: lane l holds B[8*(l/16) + j][l % 16], j = 0..7
 //     C: lane l holds C[4*(l/16) + i][l % 16], i = 0..3   (4 floats per lane)
+//   v_mfma_f32_32x32x16_{f16,bf16}  C[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l % 32][8*(l/32) + j], j = 0..7
+//     B: lane l holds B[8*(l/32) + j][l % 32], j = 0..7
+//     C: lane l holds C[8*g + 4*(l/32) + i][l % 32] at element 4*g + i, g, i = 0..3
 // The reduction index k only has to be enumerated the same way in A and B, so the
 // kernels are free to permute it consistently (the P.V product relies on this).
 //
@@ -23,6 +27,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -43,6 +48,9 @@ template <> struct Op<F16> {
   typedef half8 vec;
   static __device__ __forceinline__ float4v mfma(const vec& a, const vec& b, const float4v& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float16v mfma32(const vec& a, const vec& b, const float16v& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   // Round-to-nearest-even fp32 -> fp16 (v_cvt_f16_f32 under the default rounding mode).
   static __device__ __forceinline__ uint16_t from_float(float x) {
@@ -65,6 +73,9 @@ template <> struct Op<BF16> {
   typedef bf16x8 vec;
   static __device__ __forceinline__ float4v mfma(const vec& a, const vec& b, const float4v& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float16v mfma32(const vec& a, const vec& b, const float16v& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   // Round-to-nearest-even fp32 -> bf16 (gfx950 converts natively).
   static __device__ __forceinline__ uint16_t from_float(float x) {

@@ -10,11 +10,13 @@
 //   * A workgroup is 4 waves and owns 128 query rows that share one KV head: for a
 //     GQA group of G query heads it takes bq = 128 / G positions of every head of the
 //     group, so each K/V tile brought into LDS serves all G heads.
-//   * Each wave owns 32 rows (two 16-row blocks). Scores are produced transposed,
-//     S^T = K Q^T, with v_mfma_f32_16x16x32: K comes from LDS as the A operand and Q
-//     stays in registers as the B operand for the whole kernel. The accumulator then
-//     holds, per lane, one query row and 16 keys, which is exactly the B-operand
-//     layout the P.V product needs, so P never leaves registers.
+//   * Each wave owns 32 rows. Scores are produced transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16: K comes from LDS as the A operand and Q stays in registers
+//     as the B operand for the whole kernel. The accumulator then holds, per lane, one
+//     query row and 32 of the tile's keys (the other 32 sit in lane l ^ 32), which is
+//     exactly the B-operand layout the P.V product needs, so P never leaves registers.
+//     The 32x32x16 atom (rather than 16x16x32) leaves more issue slots to the softmax
+//     VALU work of the other wave on the same SIMD and halves the MFMA count.
 //   * O^T += V^T P^T with the same MFMA; the V^T operand is read from the row-major
 //     V tile with ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values
 //     on the way out of LDS. K and V are therefore stored in LDS exactly as they sit
@@ -81,31 +83,55 @@ __device__ __forceinline__ int scalar_load(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)(p);
 }
 
-// 16-byte chunk swizzle: spreads the 16 rows read by one 16-lane group over 256 bytes
-// of banks. Rows of 128 bytes (d = 64) pair up before the XOR so that two consecutive
-// rows, which already sit in opposite bank halves, share one XOR value. Only row % 16
-// (row % 32 for d = 64, through row >> 1) matters, so rows 16 apart share a pattern.
+// 16-byte chunk swizzle, chunk' = chunk ^ swz(row). It must spread two read patterns
+// over the 64 banks: the K reads (16 consecutive rows at one chunk per 16 lanes) and the
+// V transpose reads (4 consecutive rows x 4 consecutive chunks per 32 lanes). Rotating
+// the low row bits before the XOR serves both: for d >= 128 (256-byte rows) the low
+// four row bits are rotated by two; for d = 64 (two rows per 256 bytes) the three bits
+// above the row's parity are rotated by one. Only row % 16 (row % 32 for d = 64)
+// matters, so rows 16 or 32 apart share a pattern.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 64) return (row >> 1) & 7;
-  else return row & 15;
+  if constexpr (D == 64) {
+    const int k = (row >> 1) & 7;
+    return ((k & 1) << 2) | (k >> 1);
+  } else {
+    const int r = row & 15;
+    return ((r & 3) << 2) | (r >> 2);
+  }
 }
 
-template <int D, typename T, bool PRECISE>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void prefill_kernel(const PrefillParams p) {
-  constexpr int KS = D / 32;            // k-steps of the S^T product
-  constexpr int DB = D / 16;            // 16-wide d blocks of O^T
+// NG groups of four waves per workgroup. With NG = 2 both groups own the same 128 query
+// rows and split the workgroup's key tiles between them, merging their (o, m, l) at the
+// end; this halves the longest workgroup when there are too few workgroups to balance
+// the causal triangle. Each group has its own two LDS stages.
+template <int D, int NG, typename T, bool PRECISE>
+__global__ __launch_bounds__(kThreads * NG, D == 256 ? 1 : 2)
+void prefill_kernel(const PrefillParams p) {
+  constexpr int KS = D / 16;            // k-steps (16 deep) of the S^T product
+  constexpr int DB = D / 32;            // 32-wide d blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 512 / D;          // rows covered by one 1 KiB wave-wide LDS copy
   constexpr int NIW = kPage / RPI / kWaves;   // such copies per wave per tile (K and V each)
   constexpr int TILE = kPage * D;       // elements per K (or V) tile
   constexpr int ROWB = D * 2;           // bytes per LDS row
-  extern __shared__ __align__(16) uint16_t smem[];   // [2 stages][K, V][TILE]
+  __shared__ __align__(16) uint16_t smem[NG * 2 * 2 * TILE];   // [group][2 stages][K, V][TILE]
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int qblk = gridDim.x - 1 - blockIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = tid >> 8, wave = (tid >> 6) & 3;   // key-range group, wave inside the group
+  const int lq = lane & 31, half = lane >> 5;        // query column, k-half of the 32x32 layouts
+
+  // The dispatcher hands workgroups to the 8 XCDs round-robin. Workgroup x is given work
+  // item `lid` so that each XCD walks a contiguous run of items: the query blocks of one
+  // (sequence, KV head) in a row, heaviest (last) first. Workgroups resident on an XCD at
+  // the same time then stream the same K/V through its L2, and the longest causal blocks
+  // start first.
+  const int nx = gridDim.x, xcd = blockIdx.x & 7, per = nx >> 3, extra = nx & 7;
+  const int lid = xcd * per + min(xcd, extra) + (int)(blockIdx.x >> 3);
+  const int nq = (p.seqlen_q + p.bq - 1) / p.bq;
+  const int qblk = nq - 1 - lid % nq;
+  const int bh = lid / nq;
+  const int b = bh % p.batch, kvh = bh / p.batch;
 
   int L = p.seqlen_k;
   if (p.seqlens_k) L = min(max(scalar_load(p.seqlens_k + b), 0), p.seqlen_k);
@@ -113,30 +139,29 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void prefill_kernel(con
   const int off = L - p.seqlen_q;       // bottom-right alignment of the causal mask
   const float c = p.scale_log2;
 
-  // ---- this lane's two query rows (one per 16-row block) and their Q fragments
-  int rpos[2], rh[2];
-  bool rok[2];
-  u32x4 qf[2][KS];
+  // ---- this lane's query row and its Q fragments (B operand of S^T)
+  const int r = wave * 32 + lq;
+  const int hig = r / p.bq;
+  const int rpos = q0 + (r - hig * p.bq);
+  const int rh = kvh * p.group + hig;
+  const bool rok = hig < p.group && rpos < p.seqlen_q;
+  u32x4 qf[KS];
+  {
+    const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (int64_t)rpos * p.q_ss;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = wave * 32 + qb * 16 + lr;
-    const int hig = r / p.bq;
-    rpos[qb] = q0 + (r - hig * p.bq);
-    rh[qb] = kvh * p.group + hig;
-    rok[qb] = hig < p.group && rpos[qb] < p.seqlen_q;
-    const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh[qb] * p.q_sh + (int64_t)rpos[qb] * p.q_ss;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[qb][s] = rok[qb] ? ldg16(qp + s * 32 + lg * 8) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < KS; ++s) qf[s] = rok ? ldg16(qp + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
   }
 
-  // ---- tile range: [0, n_full) need no masking, [n_full, n_tiles) straddle a boundary
+  // ---- tile range: [0, n_full) need no masking, [n_full, n_tiles) straddle a boundary;
+  // group g takes tiles [g*h, min((g+1)*h, n_tiles)), h = ceil(n_tiles / NG)
   const int pmax = min(q0 + p.bq, p.seqlen_q) - 1;
   const int kv_end = p.causal ? min(L, pmax + off + 1) : L;
   const int n_tiles = kv_end > 0 ? (kv_end + kPage - 1) / kPage : 0;
   int n_full = L / kPage;
   if (p.causal) n_full = min(n_full, max(q0 + off + 1, 0) / kPage);
   n_full = min(n_full, n_tiles);
+  const int h = (n_tiles + NG - 1) / NG;
+  const int j0 = grp * h, j1 = min(n_tiles, j0 + h);
 
   // ---- per-lane constants of the K/V copies (byte offsets inside a tile's rows)
   const bool paged = p.block_table != nullptr;
@@ -145,13 +170,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void prefill_kernel(con
   uint32_t dma_off[NIW];
 #pragma unroll
   for (int k = 0; k < NIW; ++k) {
-    const int r = (wave * NIW + k) * RPI + r_in;
-    dma_off[k] = (uint32_t)((r * rs + ((pc ^ swz<D>(r)) << 3)) * 2);
+    const int row = (wave * NIW + k) * RPI + r_in;
+    dma_off[k] = (uint32_t)((row * rs + ((pc ^ swz<D>(row)) << 3)) * 2);
   }
-  const uint32_t smem_base = lds_addr(smem);
+  const uint32_t smem_base = lds_addr(smem) + grp * 2 * 2 * TILE * 2;
+  const char* gsmem = reinterpret_cast<const char*>(smem) + grp * 2 * 2 * TILE * 2;
 
-  // Copy tile j into LDS stage `stage`. Rows past the key length, and every row of a page
-  // whose id is out of range, are fetched from the zero block instead.
+  // Copy tile j into this group's LDS stage `stage`. Rows past the key length, and every
+  // row of a page whose id is out of range, are fetched from the zero block instead.
   auto issue_tile = [&](int j, int stage) {
     int64_t base;
     bool page_ok = true;
@@ -183,143 +209,131 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void prefill_kernel(con
   };
 
   // ---- per-lane LDS read offsets (bytes inside a stage's K or V tile)
-  // K A-operand for S^T: row kb*16 + lr, chunk 4*st + lg (kb enters as an immediate).
+  // K A-operand for S^T: row 32*kb + lq (kb enters as an immediate), chunk 2*s + half.
   uint32_t koff[KS];
 #pragma unroll
-  for (int st = 0; st < KS; ++st) koff[st] = lr * ROWB + (((st * 4 + lg) ^ swz<D>(lr)) << 4);
-  // V^T A-operand via transpose reads: lane (lg, lr) addresses row 4*lg + lr/4 (+16, +32)
-  // at column 16*db + 4*(lr % 4).
-  const int vrow = 4 * lg + (lr >> 2);
-  uint32_t voff[DB];
+  for (int s = 0; s < KS; ++s) koff[s] = lq * ROWB + (((2 * s + half) ^ swz<D>(lq)) << 4);
+  // V^T A-operand via transpose reads: lane (g = lane/16, j = lane%16) addresses row
+  // 16*t + 8*h + 4*(g/2) + j/4 (t enters as an immediate) at column 32*db + 16*(g%2) + 4*(j%4).
+  const int tg = lane >> 4, tj = lane & 15;
+  uint32_t voff[2][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int chunk = 2 * db + ((lr & 3) >> 1);
-    voff[db] = vrow * ROWB + ((chunk ^ swz<D>(vrow)) << 4) + 8 * (lr & 1);
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = 8 * hh + 4 * (tg >> 1) + (tj >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + 16 * (tg & 1) + 4 * (tj & 3);
+      voff[hh][db] = row * ROWB + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+    }
   }
 
-  float mref[2] = {-INFINITY, -INFINITY};   // reference max (log2 domain) of o and l
-  float lsum[2] = {0.f, 0.f};               // this lane's share of l
-  float4v acc[DB][2];
+  float mref = -INFINITY;   // reference max (log2 domain) behind o and l
+  float lsum = 0.f;         // this lane's share of l (its 32 keys of each tile)
+  float16v acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = float4v{0, 0, 0, 0};
+  for (int db = 0; db < DB; ++db) acc[db] = float16v{};
 
-  // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto step = [&](int j, auto stage_c, auto mask_c) {
+  // One tile from stage STAGE of this group: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto compute = [&](int j, auto stage_c, auto mask_c) {
     constexpr int STAGE = decltype(stage_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (j + 1 < n_tiles) issue_tile(j + 1, STAGE ^ 1);
-    const char* ks = reinterpret_cast<const char*>(smem) + STAGE * 2 * TILE * 2;
+    const char* ks = gsmem + STAGE * 2 * TILE * 2;
     const char* vs = ks + TILE * 2;
 
-    float4v s[4][2];
+    // scores of keys 32*kb + 8*g + 4*half + i, at sc[kb][4*g + i]
+    float16v sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb][0] = s[kb][1] = float4v{0, 0, 0, 0};
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = float16v{};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + koff[st] + kb * 16 * ROWB);
-        s[kb][0] = Op<T>::mfma(as_op<T>(a), as_op<T>(qf[0][st]), s[kb][0]);
-        s[kb][1] = Op<T>::mfma(as_op<T>(a), as_op<T>(qf[1][st]), s[kb][1]);
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + koff[s] + kb * 32 * ROWB);
+        sc[kb] = Op<T>::mfma32(as_op<T>(a), as_op<T>(qf[s]), sc[kb]);
       }
     }
 
-    float mt[2];
+    if constexpr (MASK) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if constexpr (MASK) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = j * kPage + kb * 16 + lg * 4 + i;
-            const bool vis = key < L && (!p.causal || key <= rpos[qb] + off);
-            s[kb][qb][i] = vis ? s[kb][qb][i] : -INFINITY;
-          }
-      }
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kb | i) mx = fmaxf(mx, s[kb][qb][i]);
-      mt[qb] = rows4_max(mx) * c;
-    }
-    const bool up0 = mt[0] > mref[0] + kLazy, up1 = mt[1] > mref[1] + kLazy;
-    if (__builtin_amdgcn_ballot_w64(up0 || up1) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const bool up = qb ? up1 : up0;
-        const float nref = up ? mt[qb] : mref[qb];
-        const float alpha = up ? fast_exp2(mref[qb] - nref) : 1.f;
-        mref[qb] = nref;
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-      }
-    }
-
-    u32x4 pf[2][2];
-    u32x4 pl[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float mneg = mref[qb] == -INFINITY ? 0.f : -mref[qb];
-      float x[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[kb][i] = fast_exp2(__builtin_fmaf(s[kb][qb][i], c, mneg));
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const float* a0 = x[2 * s2];
-        const float* a1 = x[2 * s2 + 1];
-        pf[qb][s2] = u32x4{pack2<T>(a0[0], a0[1]), pack2<T>(a0[2], a0[3]),
-                           pack2<T>(a1[0], a1[1]), pack2<T>(a1[2], a1[3])};
-        if constexpr (PRECISE) {
-          float r0[4], r1[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            r0[i] = a0[i] - Op<T>::to_float(Op<T>::from_float(a0[i]));
-            r1[i] = a1[i] - Op<T>::to_float(Op<T>::from_float(a1[i]));
-          }
-          pl[qb][s2] = u32x4{pack2<T>(r0[0], r0[1]), pack2<T>(r0[2], r0[3]),
-                             pack2<T>(r1[0], r1[1]), pack2<T>(r1[2], r1[3])};
+        for (int e = 0; e < 16; ++e) {
+          const int key = j * kPage + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
+          const bool vis = key < L && (!p.causal || key <= rpos + off);
+          sc[kb][e] = vis ? sc[kb][e] : -INFINITY;
         }
-      }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kb | e) mx = fmaxf(mx, sc[kb][e]);
+    const float mt = wave_max_xor(mx, 32) * c;
+
+    // online softmax with a lazily moved reference maximum: o and l are kept relative to
+    // mref, which only moves (rescaling o and l by 2^(old - new)) when the row maximum
+    // exceeds it by more than kLazy, so every p stays <= 2^kLazy.
+    const bool up = mt > mref + kLazy;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float nref = up ? mt : mref;
+      const float alpha = up ? fast_exp2(mref - nref) : 1.f;
+      mref = nref;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+
+    const float mneg = mref == -INFINITY ? 0.f : -mref;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[kb][e] = fast_exp2(__builtin_fmaf(sc[kb][e], c, mneg));
+
+    // P^T B-operand of key step t (keys 16t..16t+15): elements 8*(t%2) .. +7 of sc[t/2]
+    u32x4 pf[4];
+    u32x4 pl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float16v& x = sc[t >> 1];
+      const int e0 = 8 * (t & 1);
+      pf[t] = u32x4{pack2<T>(x[e0], x[e0 + 1]), pack2<T>(x[e0 + 2], x[e0 + 3]),
+                    pack2<T>(x[e0 + 4], x[e0 + 5]), pack2<T>(x[e0 + 6], x[e0 + 7])};
       if constexpr (PRECISE) {
-        float ps = 0.f;
+        float rr[8];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ps += x[kb][i];
-        lsum[qb] += ps;
-      } else {
-        float ps0 = lsum[qb], ps1 = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          ps0 = Op<T>::sum2(pf[qb][s2][0], ps0);
-          ps1 = Op<T>::sum2(pf[qb][s2][1], ps1);
-          ps0 = Op<T>::sum2(pf[qb][s2][2], ps0);
-          ps1 = Op<T>::sum2(pf[qb][s2][3], ps1);
-        }
-        lsum[qb] = ps0 + ps1;
+        for (int i = 0; i < 8; ++i) rr[i] = x[e0 + i] - Op<T>::to_float(Op<T>::from_float(x[e0 + i]));
+        pl[t] = u32x4{pack2<T>(rr[0], rr[1]), pack2<T>(rr[2], rr[3]),
+                      pack2<T>(rr[4], rr[5]), pack2<T>(rr[6], rr[7])};
       }
+    }
+    if constexpr (PRECISE) {
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ps += sc[kb][e];
+      lsum += ps;
+    } else {
+      float ps0 = lsum, ps1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ps0 = Op<T>::sum2(pf[t][0], ps0);
+        ps1 = Op<T>::sum2(pf[t][1], ps1);
+        ps0 = Op<T>::sum2(pf[t][2], ps0);
+        ps1 = Op<T>::sum2(pf[t][3], ps1);
+      }
+      lsum = ps0 + ps1;
     }
 
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + voff[db] + s2 * 32 * ROWB));
-        const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + voff[db] + (s2 * 32 + 16) * ROWB));
+        const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + voff[0][db] + 16 * t * ROWB));
+        const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + voff[1][db] + 16 * t * ROWB));
         const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        acc[db][0] = Op<T>::mfma(as_op<T>(a), as_op<T>(pf[0][s2]), acc[db][0]);
-        acc[db][1] = Op<T>::mfma(as_op<T>(a), as_op<T>(pf[1][s2]), acc[db][1]);
-        if constexpr (PRECISE) {
-          acc[db][0] = Op<T>::mfma(as_op<T>(a), as_op<T>(pl[0][s2]), acc[db][0]);
-          acc[db][1] = Op<T>::mfma(as_op<T>(a), as_op<T>(pl[1][s2]), acc[db][1]);
-        }
+        acc[db] = Op<T>::mfma32(as_op<T>(a), as_op<T>(pf[t]), acc[db]);
+        if constexpr (PRECISE) acc[db] = Op<T>::mfma32(as_op<T>(a), as_op<T>(pl[t]), acc[db]);
       }
     }
   };
@@ -329,32 +343,65 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void prefill_kernel(con
   using Full = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
 
-  if (n_tiles > 0) issue_tile(0, 0);
-  int j = 0;
-  for (; j + 1 < n_full; j += 2) {
-    step(j, S0{}, Full{});
-    step(j + 1, S1{}, Full{});
-  }
-  if (j < n_full) {
-    step(j, S0{}, Full{});
-    ++j;
-  }
-  for (; j < n_tiles; ++j) {
-    if (j & 1) step(j, S1{}, Masked{});
-    else step(j, S0{}, Masked{});
+  // Step i of the workgroup: both groups take their i-th tile in lockstep (one barrier per
+  // step publishes the stage and recycles the other); a group whose range is exhausted
+  // only joins the barriers.
+  auto step = [&](int i, auto stage_c) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    const int j = j0 + i;
+    if (j + 1 < j1) issue_tile(j + 1, STAGE ^ 1);
+    if (j < n_full) compute(j, stage_c, Full{});
+    else if (j < j1) compute(j, stage_c, Masked{});
+  };
+
+  if (j0 < j1) issue_tile(j0, 0);
+  for (int i = 0; i < h; i += 2) {
+    step(i, S0{});
+    if (i + 1 < h) step(i + 1, S1{});
   }
 
-  // ---- epilogue: O = o / l, lse = ln 2 * (mref + log2 l)
+  if constexpr (NG == 2) {
+    // Hand group 1's (o, m, l) to group 0 through LDS and merge them there:
+    // M = max(m0, m1), o = 2^(m0-M) o0 + 2^(m1-M) o1, l likewise.
+    constexpr int STRIDE = (DB * 16 + 2) * 64;     // floats per wave
+    float* xb = reinterpret_cast<float*>(smem) + wave * STRIDE + lane;
+    __syncthreads();
+    if (grp == 1) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float l = rows4_sum(lsum[qb]);
-    if (!rok[qb]) continue;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t ob = b * p.o_sb + (int64_t)rh[qb] * p.o_sh + (int64_t)rpos[qb] * p.o_ss;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d0 = db * 16 + lg * 4;
-      const float4v v = acc[db][qb] * inv;
+        for (int e = 0; e < 16; ++e) xb[(db * 16 + e) * 64] = acc[db][e];
+      xb[DB * 16 * 64] = mref;
+      xb[(DB * 16 + 1) * 64] = lsum;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xb[DB * 16 * 64];
+    const float l1 = xb[(DB * 16 + 1) * 64];
+    const float M = fmaxf(mref, m1);
+    const float w0 = mref == -INFINITY ? 0.f : fast_exp2(mref - M);
+    const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][e] = w0 * acc[db][e] + w1 * xb[(db * 16 + e) * 64];
+    lsum = w0 * lsum + w1 * l1;
+    mref = M;
+  }
+
+  // ---- epilogue: O = o / l, lse = ln 2 * (mref + log2 l); lane holds d = 32*db + 8*g + 4*half + i
+  const float l = wave_sum_xor(lsum, 32);
+  if (!rok) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (int64_t)rpos * p.o_ss;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * half;
+      const float4v v = float4v{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]} * inv;
       if (p.o_dtype == kF32) {
         *reinterpret_cast<float4v*>(static_cast<float*>(p.o) + ob + d0) = v;
       } else if (p.o_dtype == kF16) {
@@ -365,25 +412,31 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void prefill_kernel(con
             u32x2{pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3])};
       }
     }
-    if (p.lse && lg == 0)
-      p.lse[((int64_t)b * p.hq + rh[qb]) * p.seqlen_q + rpos[qb]] =
-          l > 0.f ? (mref[qb] + __log2f(l)) * kLn2 : -INFINITY;
   }
+  if (p.lse && half == 0)
+    p.lse[((int64_t)b * p.hq + rh) * p.seqlen_q + rpos] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// Below this many single-group workgroups (four rounds of two per CU on 256 CUs) the
+// key range of each workgroup is split over two groups (d <= 128).
+constexpr int64_t kSplitBelow = 2048;
+
+template <int D, int NG, typename T, bool PRECISE>
+hipError_t launch_ng(const PrefillParams& p, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<D, NG, T, PRECISE>), dim3((unsigned)blocks),
+                     dim3(kThreads * NG), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <int D, typename T, bool PRECISE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  const size_t lds = 2 * 2 * kPage * D * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, T, PRECISE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  const int64_t nq = (p.seqlen_q + p.bq - 1) / p.bq;
+  const int64_t blocks = nq * p.hkv * p.batch;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if constexpr (D <= 128) {
+    if (blocks < kSplitBelow) return launch_ng<D, 2, T, PRECISE>(p, blocks, stream);
   }
-  const dim3 grid((p.seqlen_q + p.bq - 1) / p.bq, p.hkv, p.batch);
-  hipLaunchKernelGGL((prefill_kernel<D, T, PRECISE>), grid, dim3(kThreads), lds, stream, p);
-  return hipGetLastError();
+  return launch_ng<D, 1, T, PRECISE>(p, blocks, stream);
 }
 
 template <int D>

@@ -116,3 +116,25 @@ def test_prefill_deterministic():
     a, _ = gpu_prefill(inp)
     b, _ = gpu_prefill(inp)
     np.testing.assert_array_equal(a, b)
+
+
+# Launches of at least 2048 workgroups run the single-group kernel (each workgroup walks
+# its whole key range); the small cases above all run the two-group form.
+ONE_GROUP = [
+    P("f16_d64_causal_paged_2048wg", 4, 64, 64, 1024, 1024, 64, "f16", True, "paged"),
+    P("bf16_d128_noncausal_dense_2048wg", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense",
+      seqlens_k=(1100, 1000, 999, 64, 1, 700, 1100, 130)),
+]
+
+
+@pytest.mark.parametrize("case", ONE_GROUP, ids=lambda c: c.name)
+def test_prefill_one_group_sampled(case):
+    say(f"prefill parity (sampled rows) {case}")
+    inp = make_prefill_inputs(case, seed=5)
+    O, _ = gpu_prefill(inp)
+    rows = np.unique(np.concatenate([[0, 31, 32, 63, 64, 127, 128, case.seqlen_q - 1],
+                                     np.random.default_rng(1).choice(case.seqlen_q, 24, replace=False)]))
+    Oref, _ = oracle_prefill(inp, q_index=rows)
+    err = max_abs_err(O[:, rows], Oref)
+    say(f"  max abs err {err:.3e} over {rows.size} rows x all (b, h)")
+    assert err <= tolerance(case)
