@@ -6,6 +6,9 @@
 //     A: lane l holds A[l % 16][8*(l/16) + j], j = 0..7   (8 halves per lane)
 //     B: lane l holds B[8*(l/16) + j][l % 16], j = 0..7
 //     C: lane l holds C[4*(l/16) + i][l % 16], i = 0..3   (4 floats per lane)
+//   v_mfma_f32_16x16x16_{f16,bf16}  C[16x16] += A[16x16] * B[16x16]
+//     A: lane l holds A[l % 16][4*(l/16) + j], j = 0..3;  B: lane l holds B[4*(l/16) + j][l % 16]
+//     C: as for 16x16x32
 //   v_mfma_f32_32x32x16_{f16,bf16}  C[32x32] += A[32x16] * B[16x32]
 //     A: lane l holds A[l % 32][8*(l/32) + j], j = 0..7
 //     B: lane l holds B[8*(l/32) + j][l % 32], j = 0..7
@@ -24,6 +27,7 @@
 namespace attn {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
@@ -68,6 +72,11 @@ template <> struct Op<F16> {
   static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pair), half2v{1, 1}, acc, false);
   }
+  // v_mfma_f32_16x16x16_f16 on four 16-bit values per lane held in two dwords.
+  static __device__ __forceinline__ float4v mfma16k(const u32x2& a, const u32x2& b, const float4v& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4, a), __builtin_bit_cast(half4, b), c,
+                                                0, 0, 0);
+  }
 };
 template <> struct Op<BF16> {
   typedef bf16x8 vec;
@@ -93,6 +102,11 @@ template <> struct Op<BF16> {
   static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2v, pair),
                                           short2v{0x3F80, 0x3F80}, acc, false);
+  }
+  // v_mfma_f32_16x16x16_bf16 on four 16-bit values per lane held in two dwords.
+  static __device__ __forceinline__ float4v mfma16k(const u32x2& a, const u32x2& b, const float4v& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                    __builtin_bit_cast(short4v, b), c, 0, 0, 0);
   }
 };
 
@@ -125,6 +139,47 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) short4v*)(p));
   return __builtin_bit_cast(u32x2, r);
+}
+
+constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+// (vmcnt is split over bits 3:0 and 15:14 of the immediate).
+constexpr unsigned wait_vm(unsigned n) { return kWaitVm0 | (n & 15u) | ((n >> 4) << 14); }
+
+// 16 bytes of zeros in global memory: the source of every LDS row past a key length.
+static __device__ __align__(16) const uint16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// Byte address of a shared-memory location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+// global_load_lds_dwordx4 with a per-lane 64-bit address: lane l's 16 bytes land at LDS
+// byte lds + 16 * l. Issued from inline asm so that the compiler does not fence LDS reads
+// of the other stage on it; completion is awaited explicitly (vmcnt) before the barrier
+// that publishes the stage.
+__device__ __forceinline__ void dma16_v(const uint16_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// Same copy with a wave-uniform base in SGPRs and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_s(const uint16_t* base, uint32_t voff, uint32_t lds) {
+  // readfirstlane returns a signed int: widen through uint32_t so the low word is not
+  // sign-extended into the high one.
+  const uint64_t b = (uint64_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"((const uint16_t*)bs), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Read-only device int through the constant address space, so it becomes a scalar load.
+__device__ __forceinline__ int scalar_load(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(p);
 }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {

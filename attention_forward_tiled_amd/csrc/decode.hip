@@ -8,20 +8,28 @@
 // leaves a normalised O_s and lse_s = ln(sum over the split of e^(s_j)); the combine
 // weights the splits by e^(lse_s - max lse).
 //
-// How it is mapped onto CDNA4 (the split kernel streams K/V once from HBM and is
-// bandwidth-bound, so the layout choices are about bytes in flight, not flops):
-//   * One workgroup (4 waves) per (partition, KV head, sequence). The G query heads
-//     that share the KV head are processed together, so every K/V byte is read once.
-//   * Waves take whole pages round-robin inside the partition and keep their own
-//     running (m, l, o); the four states are merged through LDS at the end.
-//   * Per page, the wave issues all of its K and V loads up front (16-byte loads,
-//     each wave instruction covering whole 256-byte rows for d = 128), then computes
-//     S^T = K Q^T with v_mfma_f32_16x16x32 (Q padded to 16 columns, K loaded straight
-//     into the A-operand layout), and accumulates P.V on the vector ALUs: V rows are
-//     consumed in their natural layout, with P broadcast through a small per-wave LDS
-//     buffer.
-//   * Keys past the sequence length (NaN-poisoned page tails) load as zeros and their
-//     scores are masked, so they never reach the output.
+// How it is mapped onto CDNA4. The split kernel streams every K/V byte once from HBM
+// and does little arithmetic per byte, so its design is about keeping enough bytes in
+// flight, not about flops:
+//   * One workgroup (4 waves) per (KV head, sequence, partition), launched partition-
+//     major so that the first partitions of every sequence, which are always full,
+//     are dispatched first and the partial tail partitions fill the end of the grid.
+//     The G query heads that share the KV head are processed together, so every K/V
+//     byte is read once.
+//   * Pages stream through a ring of LDS stages (K tile and V tile of one 64-key page
+//     per stage) filled by global_load_lds_dwordx4, which needs no registers for the
+//     data in flight; the ring is several pages deep, and page i + NST - 1 is started
+//     as soon as page i is published, so up to NST - 1 pages are in flight while page
+//     i is consumed.
+//   * All four waves work on the same page, 16 keys each: S^T = K Q^T with
+//     v_mfma_f32_16x16x32 (K rows from LDS as the A operand, the group's query heads
+//     padded to 16 columns as the B operand). The accumulator layout is the B-operand
+//     layout of v_mfma_f32_16x16x16, so O^T += V^T P^T follows with P in registers and
+//     V^T read from the row-major V tile by ds_read_b64_tr_b16. Each wave keeps its own
+//     (m, l, o) per query head; the four are merged through LDS at the end.
+//   * Rows past the partition end and rows of pages whose id is out of range are
+//     copied from a block of zeros and their scores are masked, so NaN in unused page
+//     slots never reaches the output.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,22 +40,58 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-template <int D, typename T, int GT>
+// 16-byte chunk swizzle of the decode's LDS tiles, chunk' = chunk ^ dswz(row). It keeps
+// two read patterns free of bank conflicts: the K reads (16 consecutive rows at one chunk
+// per 16 lanes) and the V transpose reads (8 consecutive rows times two adjacent chunks
+// per 32 lanes). For rows of 256 bytes or more, row r maps to 2 * (r mod 8) + (r / 8 mod
+// 2): a permutation of 0..15 whose upper three bits differ inside each run of 8 rows. For
+// d = 64 (two 128-byte rows per 256 bytes) the same idea is applied to row / 2 mod 8.
+template <int D>
+__device__ __forceinline__ int dswz(int row) {
+  if constexpr (D == 64) {
+    const int k = (row >> 1) & 7;
+    return ((k & 3) << 1) | (k >> 2);
+  } else {
+    const int r = row & 15;
+    return ((r & 7) << 1) | (r >> 3);
+  }
+}
+
+// Wait until at most `ahead` pages of copies (PER wave-instructions each) are still in
+// flight for this wave; `ahead` is at most N. The count has to be an immediate.
+template <int PER, int N>
+__device__ __forceinline__ void wait_pages(int ahead) {
+  if constexpr (N <= 0) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  } else {
+    if (ahead >= N) __builtin_amdgcn_s_waitcnt(wait_vm(N * PER));
+    else wait_pages<PER, N - 1>(ahead);
+  }
+}
+
+// Ring depth: 128 KiB of K/V stages per workgroup.
+template <int D> constexpr int kDecodeStages = 512 / D;
+
+template <int D, typename T, int NST>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeParams p) {
-  constexpr int KS = D / 32;              // k-steps of S^T
-  constexpr int CPR = D / 8;              // 16-byte chunks per key row
-  constexpr int RPL = 64 / CPR;           // key rows covered by one wave-wide load
-  constexpr int VL = kPage / RPL;         // V loads per lane per page
-  __shared__ float p_lds[kWaves][kPage][GT];
-  __shared__ float st_m[kWaves][GT], st_l[kWaves][GT];
-  __shared__ float o_lds[kWaves][GT][D];
+  constexpr int KS = D / 32;                 // k-steps of S^T
+  constexpr int DB = D / 16;                 // 16-wide d blocks of O^T
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int RPI = 512 / D;               // rows per 1 KiB wave-wide copy
+  constexpr int NIW = kPage / RPI / kWaves;  // such copies per wave per tile (K and V each)
+  constexpr int ROWB = D * 2;                // bytes per LDS row
+  constexpr int TILE_B = kPage * ROWB;       // bytes per K (or V) tile
+  constexpr int OSTR = D + 4;                // floats per row of the merge buffer (padded)
+  static_assert(NST >= 2 && (NST - 2) * 2 * NIW < 64, "ring depth");
+  static_assert(kWaves * 16 * OSTR * 4 + 2 * kWaves * 16 * 4 <= NST * 2 * TILE_B, "merge buffer");
+  __shared__ __align__(16) char ring[NST * 2 * TILE_B];   // [stage][K, V][64 rows][D]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int G = p.group;
 
-  const int L = min(max(p.seqlens_k[b], 0), p.max_seqlen_k);
+  const int L = min(max(scalar_load(p.seqlens_k + b), 0), p.max_seqlen_k);
   const int start = split * p.part_tokens;
   const int end = min(start + p.part_tokens, L);
   const int64_t out_row0 = ((int64_t)b * p.hq + (int64_t)kvh * G) * p.num_splits + split;
@@ -61,7 +105,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
     return;
   }
 
-  // Q fragments (B operand): lane lr holds query head lr of the group (zero if lr >= G).
+  // Q fragments (B operand of S^T): lane lr holds query head lr of the group (zero if
+  // lr >= G). They are waited for here, before any copy is started, so that the wait
+  // the compiler places before their first use does not also drain the copies.
   u32x4 qf[KS];
   {
     const bool ok = lr < G;
@@ -69,144 +115,143 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = ok ? ldg16(qp + s * 32 + lg * 8) : u32x4{0, 0, 0, 0};
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-  const int vrow = lane / CPR, vch = lane % CPR;  // this lane's V row offset / chunk
-  float m = -INFINITY, lsum = 0.f;                 // S^T layout: query lr
-  float acc[GT][8];                                // P.V layout: queries x 8 d of chunk vch
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-
-  const int first_page = start / kPage;
+  const int first_page = start / kPage;            // start is a multiple of the page size
   const int n_pages = (end - start + kPage - 1) / kPage;
-  const int64_t row_stride = (int64_t)p.hkv * D;
+  const int64_t rs = (int64_t)p.hkv * D;           // elements between key rows of a page
+  const int32_t* table = p.block_table + (int64_t)b * p.max_blocks + first_page;
 
-  for (int pi = wave; pi < n_pages; pi += kWaves) {
-    const int lp = first_page + pi;
-    const int key0 = lp * kPage;
-    const int pg = p.block_table[(int64_t)b * p.max_blocks + lp];
+  // per-lane byte offsets of the copies inside a page (row-major, swizzled chunks)
+  const int r_in = lane / CPR, pc = lane % CPR;
+  uint32_t dma_off[NIW];
+#pragma unroll
+  for (int k = 0; k < NIW; ++k) {
+    const int row = (wave * NIW + k) * RPI + r_in;
+    dma_off[k] = (uint32_t)((row * rs + ((pc ^ dswz<D>(row)) << 3)) * 2);
+  }
+  const uint32_t ring_base = lds_addr(ring);
+  uint32_t page_ok_bits = 0;   // bit (k mod 32): page k of this partition has a valid id
+
+  // Start the copies of page k into stage k % NST.
+  auto issue = [&](int k) __attribute__((always_inline)) {
+    const int pg = scalar_load(table + k);
     const bool page_ok = pg >= 0 && pg < p.num_blocks;
-    const int n_valid = page_ok ? min(kPage, end - key0) : 0;
-    const int64_t base = (int64_t)(page_ok ? pg : 0) * kPage * row_stride + (int64_t)kvh * D;
-
-    u32x4 kf[4][KS];
+    page_ok_bits = (page_ok_bits & ~(1u << (k & 31))) | ((uint32_t)page_ok << (k & 31));
+    const int64_t base = (int64_t)(page_ok ? pg : 0) * kPage * rs + (int64_t)kvh * D;
+    const int key0 = start + k * kPage;
+    const uint32_t ks = ring_base + (k % NST) * 2 * TILE_B;
+    const uint32_t vs = ks + TILE_B;
+    if (page_ok && key0 + kPage <= end) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int row = kb * 16 + lr;
-      const bool ok = row < n_valid;
+      for (int i = 0; i < NIW; ++i) dma16_s(p.k + base, dma_off[i], ks + (wave * NIW + i) * 1024);
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kf[kb][s] = ok ? ldg16(p.k + base + row * row_stride + s * 32 + lg * 8) : u32x4{0, 0, 0, 0};
-    }
-    u32x4 vf[VL];
+      for (int i = 0; i < NIW; ++i) dma16_s(p.v + base, dma_off[i], vs + (wave * NIW + i) * 1024);
+    } else {
 #pragma unroll
-    for (int jj = 0; jj < VL; ++jj) {
-      const int row = jj * RPL + vrow;
-      vf[jj] = row < n_valid ? ldg16(p.v + base + row * row_stride + vch * 8) : u32x4{0, 0, 0, 0};
-    }
-
-    // S^T: lane holds query lr, keys kb*16 + 4*lg + i
-    float x[4][4];
-    float mx = -INFINITY;
+      for (int i = 0; i < NIW; ++i) {
+        const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < end;
+        dma16_v(ok ? p.k + base + dma_off[i] / 2 : kZeroChunk, ks + (wave * NIW + i) * 1024);
+      }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float4v s = {0, 0, 0, 0};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) s = Op<T>::mfma(as_op<T>(kf[kb][st]), as_op<T>(qf[st]), s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb * 16 + lg * 4 + i;
-        const float v = key < n_valid ? s[i] * p.scale_log2 : -INFINITY;
-        x[kb][i] = v;
-        mx = fmaxf(mx, v);
+      for (int i = 0; i < NIW; ++i) {
+        const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < end;
+        dma16_v(ok ? p.v + base + dma_off[i] / 2 : kZeroChunk, vs + (wave * NIW + i) * 1024);
       }
     }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
+  };
+
+  // per-lane LDS read offsets inside a stage's K / V tile
+  uint32_t koff[KS];
+  {
+    const int row = 16 * wave + lr;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) koff[s] = row * ROWB + (((4 * s + lg) ^ dswz<D>(row)) << 4);
+  }
+  uint32_t voff[DB];
+  {
+    const int row = 16 * wave + 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 2 * db + ((lr & 3) >> 1);
+      voff[db] = row * ROWB + ((chunk ^ dswz<D>(row)) << 4) + 8 * (lr & 1);
+    }
+  }
+
+  // running state of query head lr over this wave's keys (log2 domain)
+  float m = -INFINITY, lsum = 0.f;
+  float4v acc[DB];   // O^T: lane holds d = 16*db + 4*lg + i of query head lr
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  for (int k = 0; k < min(NST - 1, n_pages); ++k) issue(k);
+
+  for (int i = 0; i < n_pages; ++i) {
+    wait_pages<2 * NIW, NST - 2>(min(NST - 2, n_pages - 1 - i));
+    __syncthreads();   // page i visible to every wave; stage (i - 1) % NST free again
+    if (i + NST - 1 < n_pages) issue(i + NST - 1);
+
+    const char* kt = ring + (i % NST) * 2 * TILE_B;
+    const char* vt = kt + TILE_B;
+    float4v s = {0.f, 0.f, 0.f, 0.f};   // S^T: keys 16*wave + 4*lg + j, query head lr
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      s = Op<T>::mfma(as_op<T>(*reinterpret_cast<const u32x4*>(kt + koff[st])), as_op<T>(qf[st]), s);
+
+    const bool page_ok = (page_ok_bits >> (i & 31)) & 1u;
+    const int key = start + i * kPage + 16 * wave + 4 * lg;
+    float x[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = page_ok && key + j < end ? s[j] * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[j]);
+    }
+    mx = rows4_max(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     m = m_new;
-    float ps = 0.f;
+    float pr[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
+    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    const u32x2 pb = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = fast_exp2(x[kb][i] - m_use);
-        ps += pv;
-        if (lr < GT) p_lds[wave][kb * 16 + lg * 4 + i][lr] = pv;
-      }
-    lsum = lsum * alpha + ps;
-
-    // rescale the P.V accumulators by each query's alpha (held by lane g)
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float ag = __shfl(alpha, g, 64);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(vt + voff[db]));
+      acc[db] = Op<T>::mfma16k(a, pb, acc[db] * alpha);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-#pragma unroll
-    for (int jj = 0; jj < VL; ++jj) {
-      const int row = jj * RPL + vrow;
-      float pr[GT];
-#pragma unroll
-      for (int g = 0; g < GT; ++g) pr[g] = p_lds[wave][row][g];
-      const u32x4 w = vf[jj];
-      float vv[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vv[2 * e] = Op<T>::to_float((uint16_t)(w[e] & 0xFFFFu));
-        vv[2 * e + 1] = Op<T>::to_float((uint16_t)(w[e] >> 16));
-      }
-#pragma unroll
-      for (int g = 0; g < GT; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pr[g], vv[e], acc[g][e]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // reduce over the lanes that share a V chunk (different key rows)
-#pragma unroll
-  for (int msk = CPR; msk < 64; msk <<= 1)
-#pragma unroll
-    for (int g = 0; g < GT; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] = wave_sum_xor(acc[g][e], msk);
-  lsum = wave_sum_xor(lsum, 16);
-  lsum = wave_sum_xor(lsum, 32);
-
-  if (lane < GT) {
-    st_m[wave][lane] = m;
-    st_l[wave][lane] = lsum;
+  // ---- merge the four waves' states through LDS and write the normalised partial
+  lsum = rows4_sum(lsum);
+  __syncthreads();   // every copy has landed (the last wait drained them) and been consumed
+  float* o_lds = reinterpret_cast<float*>(ring);               // [wave][16][OSTR]
+  float* st_m = o_lds + kWaves * 16 * OSTR;                   // [wave][16]
+  float* st_l = st_m + kWaves * 16;                           // [wave][16]
+  if (lg == 0) {
+    st_m[wave * 16 + lr] = m;
+    st_l[wave * 16 + lr] = lsum;
   }
-  if (vrow == 0) {
 #pragma unroll
-    for (int g = 0; g < GT; ++g)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o_lds[wave][g][vch * 8 + e] = acc[g][e];
-  }
+    for (int j = 0; j < 4; ++j) o_lds[(wave * 16 + lr) * OSTR + 16 * db + 4 * lg + j] = acc[db][j];
   __syncthreads();
 
-  // merge the four waves' states and write the normalised partial
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int g = i / D, d = i % D;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int g = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st_m[w][g]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st_m[w * 16 + g]);
     float den = 0.f, num = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float sc = st_m[w][g] == -INFINITY ? 0.f : fast_exp2(st_m[w][g] - M);
-      den += sc * st_l[w][g];
-      num += sc * o_lds[w][g][d];
+      const float mw = st_m[w * 16 + g];
+      const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      den += sc * st_l[w * 16 + g];
+      num += sc * o_lds[(w * 16 + g) * OSTR + d];
     }
     const int64_t row = out_row0 + (int64_t)g * p.num_splits;
     p.part_o[row * D + d] = den > 0.f ? num / den : 0.f;
@@ -255,12 +300,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
 
 template <int D, typename T>
 hipError_t launch_split_t(const DecodeParams& p, hipStream_t s) {
-  const dim3 grid(p.num_splits, p.hkv, p.batch);
-  if (p.group <= 1) hipLaunchKernelGGL((decode_split_kernel<D, T, 1>), grid, dim3(kThreads), 0, s, p);
-  else if (p.group <= 2) hipLaunchKernelGGL((decode_split_kernel<D, T, 2>), grid, dim3(kThreads), 0, s, p);
-  else if (p.group <= 4) hipLaunchKernelGGL((decode_split_kernel<D, T, 4>), grid, dim3(kThreads), 0, s, p);
-  else if (p.group <= 8) hipLaunchKernelGGL((decode_split_kernel<D, T, 8>), grid, dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((decode_split_kernel<D, T, 16>), grid, dim3(kThreads), 0, s, p);
+  // partition-major order: blockIdx.z is the partition
+  const dim3 grid(p.hkv, p.batch, p.num_splits);
+  hipLaunchKernelGGL((decode_split_kernel<D, T, kDecodeStages<D>>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -46,42 +46,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazy = 8.0f;          // log2-domain slack before the reference max moves
-constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched
-
-// 16 bytes of zeros in global memory: the source of every LDS row past a key length.
-__device__ __align__(16) const uint16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-
-// Byte address of a shared-memory location.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)(p);
-}
-
-// global_load_lds_dwordx4 with a per-lane 64-bit address: lane l's 16 bytes land at LDS
-// byte lds + 16 * l. Issued from inline asm so that the compiler does not fence LDS reads
-// of the other stage on it; completion is awaited explicitly (vmcnt) before the barrier
-// that publishes the stage.
-__device__ __forceinline__ void dma16_v(const uint16_t* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-
-// Same copy with a wave-uniform base in SGPRs and a per-lane 32-bit byte offset.
-__device__ __forceinline__ void dma16_s(const uint16_t* base, uint32_t voff, uint32_t lds) {
-  // readfirstlane returns a signed int: widen through uint32_t so the low word is not
-  // sign-extended into the high one.
-  const uint64_t b = (uint64_t)base;
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"((const uint16_t*)bs), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
-}
-
-// Read-only device int through the constant address space, so it becomes a scalar load.
-__device__ __forceinline__ int scalar_load(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)(p);
-}
 
 // 16-byte chunk swizzle, chunk' = chunk ^ swz(row). It must spread two read patterns
 // over the 64 banks: the K reads (16 consecutive rows at one chunk per 16 lanes) and the
