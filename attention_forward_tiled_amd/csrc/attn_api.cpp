@@ -3,6 +3,7 @@
 // status code and never lets a C++ exception escape.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -51,6 +52,25 @@ attn_status_t launch_status(hipError_t e, const char* what) {
 constexpr int64_t kMaxGridYZ = 65535;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Balanced decode plan in the workspace: {total, chunk, nwk} (256 bytes), prefix [B + 1],
+// start [kMaxStreamWG].
+constexpr int kMaxStreamWG = 1024;   // workgroups per KV head of the balanced split kernel
+size_t plan_bytes(int64_t batch) {
+  return 256 + align256((size_t)(batch + 1) * sizeof(int32_t)) + align256(kMaxStreamWG * sizeof(int32_t));
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
 
 }  // namespace
 
@@ -150,7 +170,8 @@ size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_heads_q, int32_t n
   if (batch <= 0 || num_heads_q <= 0 || num_splits <= 0 || num_splits > ATTN_MAX_SPLITS || !valid_d(head_dim))
     return 0;
   const size_t rows = (size_t)batch * num_heads_q * num_splits;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float)) +
+         plan_bytes(batch);
 }
 
 attn_status_t attn_splitkv_combine(const attn_combine_args_t* a, void* stream) {
@@ -220,9 +241,15 @@ attn_status_t attn_decode_fwd(const attn_decode_args_t* a, void* stream) {
       return fail(ATTN_ERR_INVALID_ARG, "workspace has %zu bytes, needs %zu", a->workspace_bytes, need);
 
     const int64_t rows = (int64_t)a->batch * a->num_heads_q * a->num_splits;
-    float* part_o = static_cast<float*>(a->workspace);
-    float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) +
-                                               align256((size_t)rows * a->head_dim * sizeof(float)));
+    char* ws = static_cast<char*>(a->workspace);
+    float* part_o = reinterpret_cast<float*>(ws);
+    const size_t lse_off = align256((size_t)rows * a->head_dim * sizeof(float));
+    float* part_lse = reinterpret_cast<float*>(ws + lse_off);
+    const size_t plan_off = lse_off + align256((size_t)rows * sizeof(float));
+    int32_t* plan = reinterpret_cast<int32_t*>(ws + plan_off);
+    int32_t* prefix = reinterpret_cast<int32_t*>(ws + plan_off + 256);
+    int32_t* start = reinterpret_cast<int32_t*>(ws + plan_off + 256 +
+                                                align256((size_t)(a->batch + 1) * sizeof(int32_t)));
     int part = (a->max_seqlen_k + a->num_splits - 1) / a->num_splits;
     part = ((part + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE) * ATTN_PAGE_SIZE;
     if (part == 0) part = ATTN_PAGE_SIZE;
@@ -239,15 +266,30 @@ attn_status_t attn_decode_fwd(const attn_decode_args_t* a, void* stream) {
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
 
+    p.plan = plan; p.prefix = prefix; p.start = start;
+
     attn::CombineParams c{};
     c.part_o = part_o; c.part_lse = part_lse; c.o = a->o; c.lse = a->lse;
     c.pairs = a->batch * a->num_heads_q; c.num_splits = a->num_splits; c.o_dtype = a->o_dtype;
 
     if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (attn_status_t st = launch_status(attn::launch_decode_split(p, a->head_dim, a->qkv_dtype, s), "decode split");
-        st != ATTN_OK)
+    // Balanced split kernel when partitions may be cut (num_splits >= 2) and the page
+    // count per KV head fits in int32; otherwise one workgroup per fixed partition.
+    const int64_t rmax = ((int64_t)a->max_seqlen_k + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE;
+    const int cus = device_cus();
+    if (a->num_splits >= 2 && (int64_t)a->batch * rmax < (int64_t(1) << 30) && cus > 0) {
+      p.nwk = std::max(1, std::min(kMaxStreamWG, cus / a->num_heads_kv));
+      c.seqlens_k = a->seqlens_k; c.heads = a->num_heads_q; c.max_seqlen_k = a->max_seqlen_k;
+      if (attn_status_t st = launch_status(attn::launch_decode_stream(p, a->head_dim, a->qkv_dtype, s),
+                                           "decode split");
+          st != ATTN_OK)
+        return st;
+    } else if (attn_status_t st = launch_status(attn::launch_decode_split(p, a->head_dim, a->qkv_dtype, s),
+                                                "decode split");
+               st != ATTN_OK) {
       return st;
+    }
     return launch_status(attn::launch_combine(c, a->head_dim, s), "decode combine");
   } catch (...) {
     return fail(ATTN_ERR_LAUNCH, "internal error in attn_decode_fwd");

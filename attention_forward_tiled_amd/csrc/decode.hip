@@ -105,6 +105,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
     return;
   }
 
+  const int first_page = start / kPage;            // start is a multiple of the page size
+  const int n_pages = (end - start + kPage - 1) / kPage;
+  const int64_t rs = (int64_t)p.hkv * D;           // elements between key rows of a page
+  const int32_t* table = p.block_table + (int64_t)b * p.max_blocks + first_page;
+
+  // Page ids are read with scalar loads ahead of their use: the first NST - 1 here, all
+  // in flight together with the Q loads, and later ones one page ahead of the copy.
+  int pid[NST - 1];
+#pragma unroll
+  for (int k = 0; k < NST - 1; ++k) pid[k] = k < n_pages ? scalar_load(table + k) : 0;
+  int pid_next = NST - 1 < n_pages ? scalar_load(table + NST - 1) : 0;
+
   // Q fragments (B operand of S^T): lane lr holds query head lr of the group (zero if
   // lr >= G). They are waited for here, before any copy is started, so that the wait
   // the compiler places before their first use does not also drain the copies.
@@ -117,11 +129,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-  const int first_page = start / kPage;            // start is a multiple of the page size
-  const int n_pages = (end - start + kPage - 1) / kPage;
-  const int64_t rs = (int64_t)p.hkv * D;           // elements between key rows of a page
-  const int32_t* table = p.block_table + (int64_t)b * p.max_blocks + first_page;
-
   // per-lane byte offsets of the copies inside a page (row-major, swizzled chunks)
   const int r_in = lane / CPR, pc = lane % CPR;
   uint32_t dma_off[NIW];
@@ -133,9 +140,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
   const uint32_t ring_base = lds_addr(ring);
   uint32_t page_ok_bits = 0;   // bit (k mod 32): page k of this partition has a valid id
 
-  // Start the copies of page k into stage k % NST.
-  auto issue = [&](int k) __attribute__((always_inline)) {
-    const int pg = scalar_load(table + k);
+  // Start the copies of page k (physical page pg) into stage k % NST.
+  auto issue = [&](int k, int pg) __attribute__((always_inline)) {
     const bool page_ok = pg >= 0 && pg < p.num_blocks;
     page_ok_bits = (page_ok_bits & ~(1u << (k & 31))) | ((uint32_t)page_ok << (k & 31));
     const int64_t base = (int64_t)(page_ok ? pg : 0) * kPage * rs + (int64_t)kvh * D;
@@ -184,12 +190,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  for (int k = 0; k < min(NST - 1, n_pages); ++k) issue(k);
+#pragma unroll
+  for (int k = 0; k < NST - 1; ++k)
+    if (k < n_pages) issue(k, pid[k]);
 
   for (int i = 0; i < n_pages; ++i) {
     wait_pages<2 * NIW, NST - 2>(min(NST - 2, n_pages - 1 - i));
     __syncthreads();   // page i visible to every wave; stage (i - 1) % NST free again
-    if (i + NST - 1 < n_pages) issue(i + NST - 1);
+    if (i + NST - 1 < n_pages) {
+      const int pg = pid_next;
+      if (i + NST < n_pages) pid_next = scalar_load(table + i + NST);
+      issue(i + NST - 1, pg);
+    }
 
     const char* kt = ring + (i % NST) * 2 * TILE_B;
     const char* vt = kt + TILE_B;
@@ -259,6 +271,312 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
   }
 }
 
+// Number of 64-key pages of sequence b (its key length clamped to [0, max_seqlen_k]).
+__device__ __forceinline__ int seq_pages(const DecodeParams& p, int b) {
+  const int L = min(max(scalar_load(p.seqlens_k + b), 0), p.max_seqlen_k);
+  return (L + kPage - 1) / kPage;
+}
+
+// Plan of the balanced decode (one workgroup of 1024 threads). The work of one KV head
+// is the concatenation of the sequences' pages ("runs", sequence-major): unit u is a
+// page of a run. The units are cut into `nwk` equal ranges of `chunk` units, one per
+// workgroup of the stream kernel; a run cut by range boundaries becomes several
+// partitions. chunk >= ceil(max pages per run / (num_splits - 1)) keeps the number of
+// partitions of any run <= num_splits. Writes prefix[b] (first unit of run b, and the
+// total at prefix[B]), start[j] (the run holding unit j * chunk) and plan = {total,
+// chunk, nwk}.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (p.batch + 1023) / 1024;
+  const int b0 = min(t * per, p.batch), b1 = min(b0 + per, p.batch);
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += seq_pages(p, b);
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan of the per-thread sums
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  const int total = part[1023];
+  int chunk = max((total + p.nwk - 1) / p.nwk, 1);
+  const int rmax = (p.max_seqlen_k + kPage - 1) / kPage;
+  if (p.num_splits > 1) chunk = max(chunk, (rmax + p.num_splits - 2) / (p.num_splits - 1));
+  int u = part[t] - sum;
+  for (int b = b0; b < b1; ++b) {
+    const int r = seq_pages(p, b);
+    p.prefix[b] = u;
+    for (int64_t j = (u + (int64_t)chunk - 1) / chunk; j * chunk < (int64_t)u + r; ++j) p.start[j] = b;
+    u += r;
+  }
+  if (t == 1023) {
+    p.prefix[p.batch] = total;
+    p.plan[0] = total;
+    p.plan[1] = chunk;
+    p.plan[2] = total > 0 ? (total + chunk - 1) / chunk : 0;
+  }
+}
+
+// Ring depth of the stream kernel: 144 KiB of stages (K tile, V tile, Q block) per
+// workgroup, so one workgroup per CU.
+template <int D> constexpr int kStreamStages = D == 64 ? 7 : (D == 128 ? 4 : 2);
+
+// Balanced (persistent) split kernel. Workgroup w serves KV head w % Hkv and unit range
+// j = w / Hkv of the plan; the workgroups of the Hkv heads with the same j walk the
+// same pages at about the same time. The pages of the range stream through the ring
+// without a break at partition boundaries; each page's stage also receives the G
+// query rows of its run (16-row block, rows >= G zero), so that no register load is
+// needed when the run changes. At the end of a partition the four waves' states are
+// merged through the stage of its last page and the partial is written to slot k of
+// its run, k = (first unit / chunk) - (run start / chunk); the workgroup that ends a run
+// marks its unused slots with lse = -inf.
+template <int D, typename T, int NST>
+__global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodeParams p) {
+  constexpr int KS = D / 32;                 // k-steps of S^T
+  constexpr int DB = D / 16;                 // 16-wide d blocks of O^T
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int RPI = 512 / D;               // rows per 1 KiB wave-wide copy
+  constexpr int NIW = kPage / RPI / kWaves;  // such copies per wave per K (or V) tile
+  constexpr int QIW = D >= 128 ? D / 128 : 1;   // copies per wave for the Q block
+  constexpr int PER = 2 * NIW + QIW;         // copies per wave per page
+  constexpr int ROWB = D * 2;                // bytes per LDS row
+  constexpr int TILE_B = kPage * ROWB;       // bytes per K (or V) tile
+  constexpr int STAGE_B = 2 * TILE_B + QIW * kWaves * 1024;
+  static_assert(NST >= 2 && (NST - 2) * PER < 64, "ring depth");
+  static_assert(3 * DB * 1024 + 2 * 3 * 64 * 4 <= STAGE_B, "merge buffer");
+  static_assert(QIW * kWaves * 1024 >= 16 * ROWB, "Q block");
+  __shared__ __align__(16) char ring[NST * STAGE_B];   // [stage][K tile, V tile, Q block]
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int kvh = blockIdx.x % p.hkv, jr = blockIdx.x / p.hkv;
+  const int G = p.group, S = p.num_splits;
+
+  const int total = scalar_load(p.plan), chunk = scalar_load(p.plan + 1);
+  if (jr >= scalar_load(p.plan + 2)) return;
+  const int u_begin = jr * chunk;
+  const int n_units = min(chunk, total - u_begin);
+
+  // Position in the unit sequence: sequence b, page `page` of its run of R pages that
+  // starts at unit U; L is the sequence's key length.
+  struct Cursor { int b, page, R, U, L; };
+  auto cursor_at = [&](int b, int u) __attribute__((always_inline)) {
+    Cursor c;
+    c.b = b;
+    c.L = min(max(scalar_load(p.seqlens_k + b), 0), p.max_seqlen_k);
+    c.R = (c.L + kPage - 1) / kPage;
+    c.U = scalar_load(p.prefix + b);
+    c.page = u - c.U;
+    return c;
+  };
+  // Step to the next unit; only called while another unit remains in the range, so a
+  // non-empty run follows.
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    if (++c.page == c.R) {
+      c.U += c.R;
+      c.page = 0;
+      do {
+        ++c.b;
+        c.L = min(max(scalar_load(p.seqlens_k + c.b), 0), p.max_seqlen_k);
+        c.R = (c.L + kPage - 1) / kPage;
+      } while (c.R == 0);
+    }
+  };
+
+  const int64_t rs = (int64_t)p.hkv * D;     // elements between key rows of a page
+  const int r_in = lane / CPR, pc = lane % CPR;
+  uint32_t dma_off[NIW];
+#pragma unroll
+  for (int k = 0; k < NIW; ++k) {
+    const int row = (wave * NIW + k) * RPI + r_in;
+    dma_off[k] = (uint32_t)((row * rs + ((pc ^ dswz<D>(row)) << 3)) * 2);
+  }
+  int q_row[QIW], q_off[QIW];   // Q block row and element offset of this lane's copies
+#pragma unroll
+  for (int k = 0; k < QIW; ++k) {
+    q_row[k] = (wave * QIW + k) * RPI + r_in;
+    q_off[k] = (pc ^ dswz<D>(q_row[k])) << 3;
+  }
+  const uint32_t ring_base = lds_addr(ring);
+  uint32_t page_ok_bits = 0;   // bit (local unit index mod 32): the page id was valid
+
+  // Start the copies of unit `k` (local index) at cursor c into stage `stage`.
+  auto issue = [&](int k, const Cursor& c, int stage) __attribute__((always_inline)) {
+    const int pg = scalar_load(p.block_table + (int64_t)c.b * p.max_blocks + c.page);
+    const bool page_ok = pg >= 0 && pg < p.num_blocks;
+    page_ok_bits = (page_ok_bits & ~(1u << (k & 31))) | ((uint32_t)page_ok << (k & 31));
+    const int64_t base = (int64_t)(page_ok ? pg : 0) * kPage * rs + (int64_t)kvh * D;
+    const int key0 = c.page * kPage;
+    const uint32_t ks = ring_base + stage * STAGE_B;
+    const uint32_t vs = ks + TILE_B;
+    const uint32_t qs = vs + TILE_B;
+    if (page_ok && key0 + kPage <= c.L) {
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) dma16_s(p.k + base, dma_off[i], ks + (wave * NIW + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) dma16_s(p.v + base, dma_off[i], vs + (wave * NIW + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < c.L;
+        dma16_v(ok ? p.k + base + dma_off[i] / 2 : kZeroChunk, ks + (wave * NIW + i) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < c.L;
+        dma16_v(ok ? p.v + base + dma_off[i] / 2 : kZeroChunk, vs + (wave * NIW + i) * 1024);
+      }
+    }
+    const uint16_t* qb = p.q + ((int64_t)c.b * p.hq + (int64_t)kvh * G) * D;
+#pragma unroll
+    for (int i = 0; i < QIW; ++i)
+      dma16_v(q_row[i] < G ? qb + q_row[i] * D + q_off[i] : kZeroChunk, qs + (wave * QIW + i) * 1024);
+  };
+
+  // per-lane LDS read offsets inside a stage
+  uint32_t koff[KS];
+  uint32_t qoff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    koff[s] = (16 * wave + lr) * ROWB + (((4 * s + lg) ^ dswz<D>(16 * wave + lr)) << 4);
+    qoff[s] = 2 * TILE_B + lr * ROWB + (((4 * s + lg) ^ dswz<D>(lr)) << 4);
+  }
+  uint32_t voff[DB];
+  {
+    const int row = 16 * wave + 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk_i = 2 * db + ((lr & 3) >> 1);
+      voff[db] = TILE_B + row * ROWB + ((chunk_i ^ dswz<D>(row)) << 4) + 8 * (lr & 1);
+    }
+  }
+
+  float m = -INFINITY, lsum = 0.f;   // state of query head lr over this wave's keys (log2)
+  float4v acc[DB];                   // O^T: lane holds d = 16*db + 4*lg + i of head lr
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const int b_first = scalar_load(p.start + jr);
+  Cursor ic = cursor_at(b_first, u_begin);   // next unit to copy
+  Cursor cc = ic;                            // unit being consumed
+  int piece_u0 = u_begin;                    // first unit of the current partition
+
+  int istage = 0;
+  const int pro = min(NST - 1, n_units);
+  for (int k = 0; k < pro; ++k) {
+    issue(k, ic, istage);
+    istage = istage + 1 == NST ? 0 : istage + 1;
+    if (k + 1 < n_units) advance(ic);
+  }
+
+  int cstage = 0;
+  for (int i = 0; i < n_units; ++i) {
+    wait_pages<PER, NST - 2>(min(NST - 2, n_units - 1 - i));
+    __syncthreads();   // unit i visible to every wave; the stage of unit i - 1 is free
+    if (i + NST - 1 < n_units) {
+      issue(i + NST - 1, ic, istage);
+      istage = istage + 1 == NST ? 0 : istage + 1;
+      if (i + NST < n_units) advance(ic);
+    }
+
+    const char* st = ring + cstage * STAGE_B;
+    float4v s = {0.f, 0.f, 0.f, 0.f};   // S^T: keys 16*wave + 4*lg + j of the page, head lr
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      s = Op<T>::mfma(as_op<T>(*reinterpret_cast<const u32x4*>(st + koff[k])),
+                      as_op<T>(*reinterpret_cast<const u32x4*>(st + qoff[k])), s);
+
+    const bool page_ok = (page_ok_bits >> (i & 31)) & 1u;
+    const int key = cc.page * kPage + 16 * wave + 4 * lg;
+    float x[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = page_ok && key + j < cc.L ? s[j] * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[j]);
+    }
+    mx = rows4_max(mx);
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    float pr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
+    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    const u32x2 pb = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(st + voff[db]));
+      acc[db] = Op<T>::mfma16k(a, pb, acc[db] * alpha);
+    }
+
+    const bool run_end = cc.page == cc.R - 1;
+    if (run_end || i == n_units - 1) {
+      // ---- end of a partition: merge the waves through this (consumed) stage
+      const float l_w = rows4_sum(lsum);
+      __syncthreads();
+      float* mb = reinterpret_cast<float*>(ring + cstage * STAGE_B);
+      float* m_lds = mb + 3 * DB * 256;
+      float* l_lds = m_lds + 3 * 64;
+      if (wave > 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<float4v*>(mb + (((wave - 1) * DB + db) * 64 + lane) * 4) = acc[db];
+        m_lds[(wave - 1) * 64 + lane] = m;
+        l_lds[(wave - 1) * 64 + lane] = l_w;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        float mw[4], lw[4];
+        mw[0] = m;
+        lw[0] = l_w;
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          mw[w] = m_lds[(w - 1) * 64 + lane];
+          lw[w] = l_lds[(w - 1) * 64 + lane];
+        }
+        const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+        float sc[4], den = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          sc[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
+          den += sc[w] * lw[w];
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const int slot = piece_u0 / chunk - cc.U / chunk;
+        const int64_t row0 = ((int64_t)cc.b * p.hq + (int64_t)kvh * G) * S;
+        if (lr < G) {
+          const int64_t row = row0 + (int64_t)lr * S + slot;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            float4v o = acc[db] * sc[0];
+#pragma unroll
+            for (int w = 1; w < 4; ++w)
+              o += *reinterpret_cast<const float4v*>(mb + (((w - 1) * DB + db) * 64 + lane) * 4) * sc[w];
+            *reinterpret_cast<float4v*>(p.part_o + row * D + 16 * db + 4 * lg) = o * inv;
+          }
+          if (lg == 0) p.part_lse[row] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+        }
+        if (run_end)   // unused partitions of the run
+          for (int e = lane; e < G * S; e += 64) {
+            const int g = e / S, sl = e % S;
+            if (sl > slot) p.part_lse[row0 + (int64_t)g * S + sl] = -INFINITY;
+          }
+      }
+      m = -INFINITY;
+      lsum = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
+      piece_u0 = u_begin + i + 1;
+    }
+    cstage = cstage + 1 == NST ? 0 : cstage + 1;
+    if (i + 1 < n_units) advance(cc);
+  }
+}
+
 // One wave per (sequence, head): lane s holds split s's lse.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p) {
@@ -267,6 +585,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
   const int pair = blockIdx.x * kWaves + wave;
   if (pair >= p.pairs) return;
   const int S = p.num_splits;
+  if (p.seqlens_k && min(scalar_load(p.seqlens_k + pair / p.heads), p.max_seqlen_k) <= 0) {
+    // a sequence with no key: no partial was written for it
+    const int64_t ob = (int64_t)pair * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (p.o_dtype == kF32) static_cast<float*>(p.o)[ob + e] = 0.f;
+      else static_cast<uint16_t*>(p.o)[ob + e] = 0;
+    }
+    if (p.lse && lane == 0) p.lse[pair] = -INFINITY;
+    return;
+  }
   const float l = lane < S ? p.part_lse[(int64_t)pair * S + lane] : -INFINITY;
   float M = l;
 #pragma unroll
@@ -311,6 +640,19 @@ hipError_t launch_split_d(const DecodeParams& p, int qkv_dtype, hipStream_t s) {
   return qkv_dtype == kF16 ? launch_split_t<D, F16>(p, s) : launch_split_t<D, BF16>(p, s);
 }
 
+template <int D, typename T>
+hipError_t launch_stream_t(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, p);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_stream_kernel<D, T, kStreamStages<D>>), dim3(p.nwk * p.hkv), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_stream_d(const DecodeParams& p, int qkv_dtype, hipStream_t s) {
+  return qkv_dtype == kF16 ? launch_stream_t<D, F16>(p, s) : launch_stream_t<D, BF16>(p, s);
+}
+
 }  // namespace
 
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, int qkv_dtype,
@@ -319,6 +661,16 @@ hipError_t launch_decode_split(const DecodeParams& p, int head_dim, int qkv_dtyp
     case 64: return launch_split_d<64>(p, qkv_dtype, stream);
     case 128: return launch_split_d<128>(p, qkv_dtype, stream);
     case 256: return launch_split_d<256>(p, qkv_dtype, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, int qkv_dtype,
+                                hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_stream_d<64>(p, qkv_dtype, stream);
+    case 128: return launch_stream_d<128>(p, qkv_dtype, stream);
+    case 256: return launch_stream_d<256>(p, qkv_dtype, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,8 +36,13 @@ struct DecodeParams {
   float* part_lse;              // [B, Hq, num_splits]
   int32_t batch, hq, hkv, group;
   int32_t num_blocks, max_blocks, max_seqlen_k, num_splits;
-  int32_t part_tokens;          // keys per split (multiple of 64)
+  int32_t part_tokens;          // keys per split (multiple of 64), partition kernel only
   float scale_log2;
+  // balanced (stream) kernel: plan written by the plan kernel into the workspace
+  int32_t* plan;                // {total units per KV head, units per workgroup, workgroups used}
+  int32_t* prefix;              // [B + 1] first unit of each sequence's run
+  int32_t* start;               // [nwk] run holding the first unit of each workgroup range
+  int32_t nwk;                  // workgroups launched per KV head
 };
 
 struct CombineParams {
@@ -45,6 +50,9 @@ struct CombineParams {
   const float* part_lse;        // [B*H, S]
   void* o;                      // [B*H, d]
   float* lse;                   // optional [B*H]
+  const int32_t* seqlens_k;     // optional [B]: sequences with no key give O = 0, lse = -inf
+  int32_t heads;                // H (to find the sequence of a (b, h) pair)
+  int32_t max_seqlen_k;
   int32_t pairs, num_splits, o_dtype;
 };
 
@@ -53,6 +61,9 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int qkv_dtype, b
                           hipStream_t stream);
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, int qkv_dtype,
                                hipStream_t stream);
+// Plan kernel then the balanced split kernel (num_splits >= 2); grid = nwk * hkv.
+hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, int qkv_dtype,
+                                hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace attn

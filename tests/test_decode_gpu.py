@@ -69,6 +69,34 @@ def test_decode_small(case, splits):
         assert np.abs(lse - lref).max() <= 1e-3
 
 
+@pytest.mark.parametrize("splits", [1, 4, 16])
+def test_decode_empty_sequences(splits):
+    # sequences with no key (reading: O = 0, lse = -inf) next to ordinary ones; the
+    # balanced split kernel never visits them, the combine writes their rows
+    case = DecodeCase("bf16_empty", 5, 8, 2, 128, "bf16", lengths_fixed=(0, 300, 0, 5000, 64))
+    inp = make_decode_inputs(case, seed=8)
+    Oref, lref = oracle_decode(inp)
+    say(f"decode with empty sequences num_splits={splits}")
+    O, lse = gpu_decode(inp, splits, with_lse=True)
+    assert max_abs_err(O, Oref) <= TOL[case.dtype]
+    empty = inp.seqlens_k == 0
+    assert (O[empty] == 0).all() and np.isneginf(lse[empty]).all() and np.isneginf(lref[empty]).all()
+    assert np.abs(lse[~empty] - lref[~empty]).max() <= 1e-3
+
+
+def test_decode_many_short_sequences():
+    # many sequences shorter than a workgroup's page range: ranges span several runs
+    lens = tuple(int(x) for x in np.random.default_rng(3).integers(1, 700, size=48))
+    case = DecodeCase("f16_many_short", 48, 8, 8, 64, "f16", lengths_fixed=lens)
+    inp = make_decode_inputs(case, seed=9)
+    Oref, lref = oracle_decode(inp)
+    for s in (2, 16):
+        say(f"decode many short sequences num_splits={s}")
+        O, lse = gpu_decode(inp, s, with_lse=True)
+        assert max_abs_err(O, Oref) <= TOL[case.dtype]
+        assert np.abs(lse - lref).max() <= 1e-3
+
+
 def test_decode_split_count_invariance():
     case = DecodeCase("inv", 3, 8, 2, 128, "bf16", lengths_fixed=(3000, 64, 1777))
     inp = make_decode_inputs(case, seed=6)
