@@ -152,6 +152,7 @@ attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
     p.seqlen_q = a->seqlen_q; p.seqlen_k = a->seqlen_k;
     p.num_blocks = a->num_blocks; p.max_blocks = a->max_blocks_per_seq;
     p.bq = 128 / G;
+    p.cus = device_cus();
     p.causal = a->causal; p.o_dtype = a->o_dtype;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;

@@ -24,6 +24,7 @@ struct PrefillParams {
   int32_t bq;                   // query positions per workgroup (rows = group * bq <= 128)
   int32_t causal, o_dtype;
   float scale_log2;             // softmax scale * log2(e)
+  int32_t cus;                  // compute units of the device (work pairing decision)
 };
 
 struct DecodeParams {

@@ -125,11 +125,15 @@ attn_status_t attn_prefill_fwd(const attn_prefill_args_t* args, void* stream);
  * Operation: the attention of attn_prefill_fwd at S_q = 1, non-causal (one query
  * attends to every key; identical to the bottom-right causal mask at S_q = 1:
  * page "gfx942 unified attention, from the math up", sections 4 and 8). The keys
- * of each sequence are split into partitions of P = roundup(ceil(max_seqlen_k /
- * num_splits), 64) tokens; one workgroup per (sequence, KV head, partition) handles
- * the G query heads of the group and writes a partial (O_s normalised, lse_s) to the
- * workspace; the combine then merges them (see attn_splitkv_combine). Both kernels
- * run on `stream` in order.
+ * of each (sequence, KV head) are split into at most num_splits partitions of whole
+ * 64-key pages; each partition yields a partial (O_s normalised, lse_s) for the G
+ * query heads of the group in the workspace, and the combine merges them (see
+ * attn_splitkv_combine). The result does not depend on the partition plan beyond
+ * rounding. With num_splits >= 2 the library chooses the partitions: a small plan
+ * kernel divides every KV head's pages into equal ranges, one per workgroup (about
+ * one workgroup per compute unit in total), and a range boundary inside a sequence
+ * starts a new partition. With num_splits = 1 each sequence is one partition. All
+ * kernels run on `stream` in order.
  *
  * Fields:
  *  q          [B, Hq, d] (the BSHD and BHSD layouts coincide at S_q = 1), qkv_dtype.
@@ -168,9 +172,10 @@ typedef struct {
 
 attn_status_t attn_decode_fwd(const attn_decode_args_t* args, void* stream);
 
-/* Bytes of decode workspace: fp32 partial outputs [B, Hq, num_splits, d] followed
- * (at a 256-byte aligned offset) by fp32 partial lse [B, Hq, num_splits]. Returns 0
- * for invalid sizes. */
+/* Bytes of decode workspace: fp32 partial outputs [B, Hq, num_splits, d], then (at
+ * 256-byte aligned offsets) fp32 partial lse [B, Hq, num_splits] and the partition
+ * plan (int32, about 4*(B + 1) + 4 KiB). Slots of unused partitions hold lse = -inf
+ * and an undefined O_s. Returns 0 for invalid sizes. */
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_heads_q, int32_t num_splits,
                                    int32_t head_dim);
 
