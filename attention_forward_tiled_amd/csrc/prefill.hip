@@ -34,6 +34,7 @@
 //     the P.V MFMA consumes).
 //   * The workgroup order is reversed over query blocks so that, under a causal
 //     mask, the longest-running blocks are dispatched first.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -68,8 +69,9 @@ __device__ __forceinline__ int swz(int row) {
 // NG groups of four waves per workgroup. With NG = 2 both groups own the same 128 query
 // rows and split the workgroup's key tiles between them, merging their (o, m, l) at the
 // end; this halves the longest workgroup when there are too few workgroups to balance
-// the causal triangle. Each group has its own two LDS stages.
-template <int D, int NG, typename T, bool PRECISE>
+// the causal triangle. Each group has its own two LDS stages. With PAIR, a workgroup
+// processes two query blocks of one (sequence, KV head) in turn (see below).
+template <int D, int NG, typename T, bool PRECISE, bool PAIR>
 __global__ __launch_bounds__(kThreads * NG, D == 256 ? 1 : 2)
 void prefill_kernel(const PrefillParams p) {
   constexpr int KS = D / 16;            // k-steps (16 deep) of the S^T product
@@ -93,39 +95,23 @@ void prefill_kernel(const PrefillParams p) {
   const int nx = gridDim.x, xcd = blockIdx.x & 7, per = nx >> 3, extra = nx & 7;
   const int lid = xcd * per + min(xcd, extra) + (int)(blockIdx.x >> 3);
   const int nq = (p.seqlen_q + p.bq - 1) / p.bq;
-  const int qblk = nq - 1 - lid % nq;
-  const int bh = lid / nq;
+  // With pairing, a workgroup takes query blocks nq - 1 - u and u of one (sequence, KV
+  // head) one after the other; under a causal mask their tile counts add up to about the
+  // same total for every u.
+  const int nu = PAIR ? (nq + 1) / 2 : nq;
+  const int unit = lid % nu;
+  const int bh = lid / nu;
   const int b = bh % p.batch, kvh = bh / p.batch;
 
   int L = p.seqlen_k;
   if (p.seqlens_k) L = min(max(scalar_load(p.seqlens_k + b), 0), p.seqlen_k);
-  const int q0 = qblk * p.bq;
   const int off = L - p.seqlen_q;       // bottom-right alignment of the causal mask
   const float c = p.scale_log2;
 
-  // ---- this lane's query row and its Q fragments (B operand of S^T)
-  const int r = wave * 32 + lq;
-  const int hig = r / p.bq;
-  const int rpos = q0 + (r - hig * p.bq);
-  const int rh = kvh * p.group + hig;
-  const bool rok = hig < p.group && rpos < p.seqlen_q;
+  // state of the current query block (set at the start of each item)
+  int q0 = 0, rpos = 0, rh = 0, n_full = 0, h = 0, j0 = 0, j1 = 0;
+  bool rok = false;
   u32x4 qf[KS];
-  {
-    const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (int64_t)rpos * p.q_ss;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = rok ? ldg16(qp + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
-  }
-
-  // ---- tile range: [0, n_full) need no masking, [n_full, n_tiles) straddle a boundary;
-  // group g takes tiles [g*h, min((g+1)*h, n_tiles)), h = ceil(n_tiles / NG)
-  const int pmax = min(q0 + p.bq, p.seqlen_q) - 1;
-  const int kv_end = p.causal ? min(L, pmax + off + 1) : L;
-  const int n_tiles = kv_end > 0 ? (kv_end + kPage - 1) / kPage : 0;
-  int n_full = L / kPage;
-  if (p.causal) n_full = min(n_full, max(q0 + off + 1, 0) / kPage);
-  n_full = min(n_full, n_tiles);
-  const int h = (n_tiles + NG - 1) / NG;
-  const int j0 = grp * h, j1 = min(n_tiles, j0 + h);
 
   // ---- per-lane constants of the K/V copies (byte offsets inside a tile's rows)
   const bool paged = p.block_table != nullptr;
@@ -194,8 +180,6 @@ void prefill_kernel(const PrefillParams p) {
   float mref = -INFINITY;   // reference max (log2 domain) behind o and l
   float lsum = 0.f;         // this lane's share of l (its 32 keys of each tile)
   float16v acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = float16v{};
 
   // One tile from stage STAGE of this group: S^T = K Q^T, online softmax, O^T += V^T P^T.
   auto compute = [&](int j, auto stage_c, auto mask_c) {
@@ -320,74 +304,117 @@ void prefill_kernel(const PrefillParams p) {
     else if (j < j1) compute(j, stage_c, Masked{});
   };
 
-  if (j0 < j1) issue_tile(j0, 0);
-  for (int i = 0; i < h; i += 2) {
-    step(i, S0{});
-    if (i + 1 < h) step(i + 1, S1{});
-  }
+  for (int it = 0; it < (PAIR ? 2 : 1); ++it) {
+    const int qblk = it == 0 ? nq - 1 - unit : unit;
+    if (it == 1 && qblk >= nq - 1 - unit) break;   // the middle block of an odd count
+    q0 = qblk * p.bq;
 
-  if constexpr (NG == 2) {
-    // Hand group 1's (o, m, l) to group 0 through LDS and merge them there:
-    // M = max(m0, m1), o = 2^(m0-M) o0 + 2^(m1-M) o1, l likewise.
-    constexpr int STRIDE = (DB * 16 + 2) * 64;     // floats per wave
-    float* xb = reinterpret_cast<float*>(smem) + wave * STRIDE + lane;
-    __syncthreads();
-    if (grp == 1) {
+    // ---- this lane's query row and its Q fragments (B operand of S^T)
+    {
+      const int r = wave * 32 + lq;
+      const int hig = r / p.bq;
+      rpos = q0 + (r - hig * p.bq);
+      rh = kvh * p.group + hig;
+      rok = hig < p.group && rpos < p.seqlen_q;
+      const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (int64_t)rpos * p.q_ss;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xb[(db * 16 + e) * 64] = acc[db][e];
-      xb[DB * 16 * 64] = mref;
-      xb[(DB * 16 + 1) * 64] = lsum;
+      for (int s = 0; s < KS; ++s) qf[s] = rok ? ldg16(qp + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
     }
-    __syncthreads();
-    if (grp == 1) return;
-    const float m1 = xb[DB * 16 * 64];
-    const float l1 = xb[(DB * 16 + 1) * 64];
-    const float M = fmaxf(mref, m1);
-    const float w0 = mref == -INFINITY ? 0.f : fast_exp2(mref - M);
-    const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[db][e] = w0 * acc[db][e] + w1 * xb[(db * 16 + e) * 64];
-    lsum = w0 * lsum + w1 * l1;
-    mref = M;
-  }
 
-  // ---- epilogue: O = o / l, lse = ln 2 * (mref + log2 l); lane holds d = 32*db + 8*g + 4*half + i
-  const float l = wave_sum_xor(lsum, 32);
-  if (!rok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (int64_t)rpos * p.o_ss;
+    // ---- tile range: [0, n_full) need no masking, [n_full, n_tiles) straddle a boundary;
+    // group g takes tiles [g*h, min((g+1)*h, n_tiles)), h = ceil(n_tiles / NG)
+    {
+      const int pmax = min(q0 + p.bq, p.seqlen_q) - 1;
+      const int kv_end = p.causal ? min(L, pmax + off + 1) : L;
+      const int n_tiles = kv_end > 0 ? (kv_end + kPage - 1) / kPage : 0;
+      n_full = L / kPage;
+      if (p.causal) n_full = min(n_full, max(q0 + off + 1, 0) / kPage);
+      n_full = min(n_full, n_tiles);
+      h = (n_tiles + NG - 1) / NG;
+      j0 = grp * h;
+      j1 = min(n_tiles, j0 + h);
+    }
+
+    mref = -INFINITY;
+    lsum = 0.f;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) acc[db] = float16v{};
+
+    if (j0 < j1) issue_tile(j0, 0);
+    for (int i = 0; i < h; i += 2) {
+      step(i, S0{});
+      if (i + 1 < h) step(i + 1, S1{});
+    }
+
+    if constexpr (NG == 2) {
+      // Hand group 1's (o, m, l) to group 0 through LDS and merge them there:
+      // M = max(m0, m1), o = 2^(m0-M) o0 + 2^(m1-M) o1, l likewise.
+      constexpr int STRIDE = (DB * 16 + 2) * 64;     // floats per wave
+      float* xb = reinterpret_cast<float*>(smem) + wave * STRIDE + lane;
+      __syncthreads();
+      if (grp == 1) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = 32 * db + 8 * g + 4 * half;
-      const float4v v = float4v{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]} * inv;
-      if (p.o_dtype == kF32) {
-        *reinterpret_cast<float4v*>(static_cast<float*>(p.o) + ob + d0) = v;
-      } else if (p.o_dtype == kF16) {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ob + d0) =
-            u32x2{pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3])};
-      } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ob + d0) =
-            u32x2{pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3])};
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xb[(db * 16 + e) * 64] = acc[db][e];
+        xb[DB * 16 * 64] = mref;
+        xb[(DB * 16 + 1) * 64] = lsum;
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const float m1 = xb[DB * 16 * 64];
+        const float l1 = xb[(DB * 16 + 1) * 64];
+        const float M = fmaxf(mref, m1);
+        const float w0 = mref == -INFINITY ? 0.f : fast_exp2(mref - M);
+        const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[db][e] = w0 * acc[db][e] + w1 * xb[(db * 16 + e) * 64];
+        lsum = w0 * lsum + w1 * l1;
+        mref = M;
       }
     }
+
+    // ---- epilogue: O = o / l, lse = ln 2 * (mref + log2 l); lane holds d = 32*db + 8*g + 4*half + i
+    const float l = wave_sum_xor(lsum, 32);
+    if (grp == 0 && rok) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (int64_t)rpos * p.o_ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * half;
+        const float4v v = float4v{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]} * inv;
+        if (p.o_dtype == kF32) {
+          *reinterpret_cast<float4v*>(static_cast<float*>(p.o) + ob + d0) = v;
+        } else if (p.o_dtype == kF16) {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ob + d0) =
+              u32x2{pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3])};
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ob + d0) =
+              u32x2{pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3])};
+        }
+      }
+    }
+    if (p.lse && half == 0)
+      p.lse[((int64_t)b * p.hq + rh) * p.seqlen_q + rpos] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+    }
+    if constexpr (PAIR) __syncthreads();   // the LDS of this item is the next item's staging area
   }
-  if (p.lse && half == 0)
-    p.lse[((int64_t)b * p.hq + rh) * p.seqlen_q + rpos] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
 }
 
-// Below this many single-group workgroups (four rounds of two per CU on 256 CUs) the
-// key range of each workgroup is split over two groups (d <= 128).
+// Below this many single-group workgroups (four rounds of two per CU on 256 CUs) a causal
+// launch splits the key range of each workgroup over two groups (d <= 128): the causal
+// triangle then leaves too few long workgroups to balance the CUs. (A non-causal launch
+// of that size keeps one group: its workgroups are all equally long, and a one-group
+// step is about 10% cheaper.)
 constexpr int64_t kSplitBelow = 2048;
 
-template <int D, int NG, typename T, bool PRECISE>
+template <int D, int NG, typename T, bool PRECISE, bool PAIR = false>
 hipError_t launch_ng(const PrefillParams& p, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, NG, T, PRECISE>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((prefill_kernel<D, NG, T, PRECISE, PAIR>), dim3((unsigned)blocks),
                      dim3(kThreads * NG), 0, stream, p);
   return hipGetLastError();
 }
@@ -398,7 +425,14 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   const int64_t blocks = nq * p.hkv * p.batch;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if constexpr (D <= 128) {
-    if (blocks < kSplitBelow) return launch_ng<D, 2, T, PRECISE>(p, blocks, stream);
+    if (p.causal && blocks < kSplitBelow) {
+      // Two-group workgroups fill a CU each. Under a causal mask, pair a heavy and a
+      // light query block per workgroup when that still leaves a workgroup per CU.
+      if (nq > 1 && blocks >= 2 * (int64_t)std::max(p.cus, 1)) {
+        return launch_ng<D, 2, T, PRECISE, true>(p, (nq + 1) / 2 * p.hkv * p.batch, stream);
+      }
+      return launch_ng<D, 2, T, PRECISE>(p, blocks, stream);
+    }
   }
   return launch_ng<D, 1, T, PRECISE>(p, blocks, stream);
 }

@@ -118,8 +118,32 @@ def test_prefill_deterministic():
     np.testing.assert_array_equal(a, b)
 
 
-# Launches of at least 2048 workgroups run the single-group kernel (each workgroup walks
-# its whole key range); the small cases above all run the two-group form.
+# Causal launches of fewer than 2048 workgroups split each workgroup's key range over two
+# groups (the small causal cases above); larger launches, and every non-causal one, run a
+# single group per workgroup. On a device with 256 compute units, causal two-group
+# launches of at least 512 query blocks also pair a heavy and a light query block per
+# workgroup; the paired cases below include an odd block count (a middle block alone).
+PAIRED = [
+    P("f16_d128_causal_paged_paired_odd", 1, 32, 8, 2080, 2080, 128, "f16", True, "paged"),
+    P("bf16_d64_causal_paged_paired_chunked", 2, 32, 8, 1030, 1100, 64, "bf16", True, "paged",
+      seqlens_k=(1100, 1057)),
+]
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: c.name)
+def test_prefill_paired_sampled(case):
+    say(f"prefill parity (paired query blocks, sampled rows) {case}")
+    inp = make_prefill_inputs(case, seed=6)
+    O, _ = gpu_prefill(inp)
+    rows = np.unique(np.concatenate([[0, 31, 32, 63, 1023, 1024, 1055, case.seqlen_q - 1],
+                                     np.random.default_rng(2).choice(case.seqlen_q, 24, replace=False)]))
+    rows = rows[rows < case.seqlen_q]
+    Oref, _ = oracle_prefill(inp, q_index=rows)
+    err = max_abs_err(O[:, rows], Oref)
+    say(f"  max abs err {err:.3e} over {rows.size} rows x all (b, h)")
+    assert err <= tolerance(case)
+
+
 ONE_GROUP = [
     P("f16_d64_causal_paged_2048wg", 4, 64, 64, 1024, 1024, 64, "f16", True, "paged"),
     P("bf16_d128_noncausal_dense_2048wg", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense",
