@@ -169,7 +169,7 @@ class DecodeWorkload:
         off = ((rows * d * 4 + 255) // 256) * 256
         self.part_lse = self.ws[off: off + rows * 4].view(torch.float32).view(B, Hq, S)
         self.comb_out = torch.empty_like(self.out)
-        self.kernel = "decode_split_kernel"
+        self.kernel = "decode_stream_kernel"
 
     def step(self):
         self.fn(self.q, self.kc, self.vc, self.bt, self.sl, max_seqlen_k=self.inp.max_seqlen_k,
