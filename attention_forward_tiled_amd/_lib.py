@@ -15,9 +15,10 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH, ATTN_ERR_N
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "LAUNCH", 4: "NO_DEVICE"}
 ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
 ATTN_BSHD, ATTN_BHSD = 0, 1
+ATTN_ROUND_RTNE, ATTN_ROUND_RTNA, ATTN_ROUND_RTZ = 0, 1, 2
 ATTN_PAGE_SIZE = 64
 ATTN_MAX_SPLITS = 64
-ATTN_ABI_VERSION = 1
+ATTN_ABI_VERSION = 2
 
 EXPORTS = ("attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes",
            "attn_splitkv_combine", "attn_last_error", "attn_abi_version", "attn_device_count")
@@ -32,7 +33,7 @@ class PrefillArgs(ctypes.Structure):
                 ("seqlen_q", _i32), ("seqlen_k", _i32), ("head_dim", _i32),
                 ("num_blocks", _i32), ("max_blocks_per_seq", _i32),
                 ("qkv_dtype", _i32), ("o_dtype", _i32), ("layout", _i32),
-                ("causal", _i32), ("precise", _i32), ("scale", _f32)]
+                ("causal", _i32), ("precise", _i32), ("scale", _f32), ("o_round", _i32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -41,13 +42,14 @@ class DecodeArgs(ctypes.Structure):
                 ("lse", _c_void_p), ("workspace", _c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("batch", _i32), ("num_heads_q", _i32), ("num_heads_kv", _i32), ("head_dim", _i32),
                 ("num_blocks", _i32), ("max_blocks_per_seq", _i32), ("max_seqlen_k", _i32),
-                ("num_splits", _i32), ("qkv_dtype", _i32), ("o_dtype", _i32), ("scale", _f32)]
+                ("num_splits", _i32), ("qkv_dtype", _i32), ("o_dtype", _i32), ("scale", _f32),
+                ("o_round", _i32)]
 
 
 class CombineArgs(ctypes.Structure):
     _fields_ = [("partial_o", _c_void_p), ("partial_lse", _c_void_p), ("o", _c_void_p),
                 ("lse", _c_void_p), ("batch", _i32), ("num_heads", _i32), ("num_splits", _i32),
-                ("head_dim", _i32), ("o_dtype", _i32)]
+                ("head_dim", _i32), ("o_dtype", _i32), ("o_round", _i32)]
 
 
 _LIB = None

@@ -16,6 +16,13 @@ from . import _lib
 
 _DT = {torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16, torch.float32: _lib.ATTN_F32}
 _LAYOUT = {"bshd": _lib.ATTN_BSHD, "bhsd": _lib.ATTN_BHSD}
+_ROUND = {"rtne": _lib.ATTN_ROUND_RTNE, "rtna": _lib.ATTN_ROUND_RTNA, "rtz": _lib.ATTN_ROUND_RTZ}
+
+
+def _round(mode: str) -> int:
+    if mode not in _ROUND:
+        raise ValueError(f"out_round must be one of {sorted(_ROUND)}")
+    return _ROUND[mode]
 
 
 class AttnError(RuntimeError):
@@ -53,7 +60,8 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
                      seqlens_k: Optional[torch.Tensor] = None, seqlen_k: Optional[int] = None,
                      layout: str = "bshd", out: Optional[torch.Tensor] = None,
                      out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
-                     scale: float = 0.0, precise: bool = False, stream=None) -> torch.Tensor:
+                     scale: float = 0.0, precise: bool = False, out_round: str = "rtne",
+                     stream=None) -> torch.Tensor:
     """Tiled attention forward. q: [B,S_q,Hq,d] (bshd) or [B,Hq,S_q,d] (bhsd).
 
     Paged K/V (block_table given): k, v are [num_blocks, 64, Hkv, d] caches and
@@ -99,7 +107,7 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     a = _lib.PrefillArgs(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(block_table), _ptr(seqlens_k),
         B, Hq, Hkv, Sq, Sk, d, num_blocks, max_blocks, _DT[q.dtype], _DT[out.dtype],
-        _LAYOUT[layout], int(bool(causal)), int(bool(precise)), float(scale))
+        _LAYOUT[layout], int(bool(causal)), int(bool(precise)), float(scale), _round(out_round))
     _check(_lib.load().attn_prefill_fwd(ctypes.byref(a), _stream(stream)))
     return out
 
@@ -113,7 +121,7 @@ def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                     num_splits: int, out: Optional[torch.Tensor] = None,
                     out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, scale: float = 0.0,
-                    stream=None) -> torch.Tensor:
+                    out_round: str = "rtne", stream=None) -> torch.Tensor:
     """Split-KV decode. q: [B, Hq, d] (or any shape with B*Hq*d elements in that order)."""
     _need(q, "q", (torch.float16, torch.bfloat16))
     _need(k_cache, "k_cache", (q.dtype,))
@@ -134,14 +142,15 @@ def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         B, Hq, Hkv, d, num_blocks, block_table.shape[1], int(max_seqlen_k), int(num_splits),
-        _DT[q.dtype], _DT[out.dtype], float(scale))
+        _DT[q.dtype], _DT[out.dtype], float(scale), _round(out_round))
     _check(_lib.load().attn_decode_fwd(ctypes.byref(a), _stream(stream)))
     return out
 
 
 def attn_splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, *,
                          out: Optional[torch.Tensor] = None, out_dtype=torch.float32,
-                         lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                         lse: Optional[torch.Tensor] = None, out_round: str = "rtne",
+                         stream=None) -> torch.Tensor:
     """Merge partials: partial_o [B, H, S, d] fp32, partial_lse [B, H, S] fp32 -> [B, H, d]."""
     _need(partial_o, "partial_o", (torch.float32,))
     _need(partial_lse, "partial_lse", (torch.float32,))
@@ -149,7 +158,7 @@ def attn_splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, *,
     if out is None:
         out = torch.empty((B, H, d), dtype=out_dtype, device=partial_o.device)
     a = _lib.CombineArgs(_ptr(partial_o), _ptr(partial_lse), _ptr(out), _ptr(lse), B, H, S, d,
-                         _DT[out.dtype])
+                         _DT[out.dtype], _round(out_round))
     _check(_lib.load().attn_splitkv_combine(ctypes.byref(a), _stream(stream)))
     return out
 

@@ -53,6 +53,15 @@ constexpr int64_t kMaxGridYZ = 65535;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Output rounding: any of the three modes for bf16, RTNE only for fp16, ignored for fp32.
+attn_status_t check_round(int32_t mode, int32_t o_dtype) {
+  if (mode != ATTN_ROUND_RTNE && mode != ATTN_ROUND_RTNA && mode != ATTN_ROUND_RTZ)
+    return fail(ATTN_ERR_INVALID_ARG, "o_round must be ATTN_ROUND_RTNE, ATTN_ROUND_RTNA or ATTN_ROUND_RTZ");
+  if (o_dtype == ATTN_F16 && mode != ATTN_ROUND_RTNE)
+    return fail(ATTN_ERR_UNSUPPORTED, "fp16 outputs are rounded to nearest even only");
+  return ATTN_OK;
+}
+
 // Balanced decode plan in the workspace: {total, chunk, nwk} (256 bytes), prefix [B + 1],
 // start [kMaxStreamWG].
 constexpr int kMaxStreamWG = 1024;   // workgroups per KV head of the balanced split kernel
@@ -97,6 +106,7 @@ attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
       return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
     if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
       return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+    if (attn_status_t st = check_round(a->o_round, a->o_dtype); st != ATTN_OK) return st;
     if (a->layout != ATTN_BSHD && a->layout != ATTN_BHSD)
       return fail(ATTN_ERR_INVALID_ARG, "layout must be ATTN_BSHD or ATTN_BHSD");
     if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -154,6 +164,7 @@ attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
     p.bq = 128 / G;
     p.cus = device_cus();
     p.causal = a->causal; p.o_dtype = a->o_dtype;
+    p.o_round = a->o_dtype == ATTN_BF16 ? a->o_round : 0;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
 
@@ -184,6 +195,7 @@ attn_status_t attn_splitkv_combine(const attn_combine_args_t* a, void* stream) {
     if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256");
     if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
       return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+    if (attn_status_t st = check_round(a->o_round, a->o_dtype); st != ATTN_OK) return st;
     const int64_t pairs = (int64_t)a->batch * a->num_heads;
     if (pairs == 0) return ok();
     if (pairs > (int64_t)1 << 30) return fail(ATTN_ERR_UNSUPPORTED, "batch * num_heads too large");
@@ -194,6 +206,7 @@ attn_status_t attn_splitkv_combine(const attn_combine_args_t* a, void* stream) {
     attn::CombineParams p{};
     p.part_o = a->partial_o; p.part_lse = a->partial_lse; p.o = a->o; p.lse = a->lse;
     p.pairs = (int32_t)pairs; p.num_splits = a->num_splits; p.o_dtype = a->o_dtype;
+    p.o_round = a->o_dtype == ATTN_BF16 ? a->o_round : 0;
     if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
     return launch_status(attn::launch_combine(p, a->head_dim, static_cast<hipStream_t>(stream)), "combine");
   } catch (...) {
@@ -209,6 +222,7 @@ attn_status_t attn_decode_fwd(const attn_decode_args_t* a, void* stream) {
       return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
     if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
       return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+    if (attn_status_t st = check_round(a->o_round, a->o_dtype); st != ATTN_OK) return st;
     if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
     if (a->num_heads_q <= 0 || a->num_heads_kv <= 0)
       return fail(ATTN_ERR_INVALID_ARG, "head counts must be positive");
@@ -272,6 +286,7 @@ attn_status_t attn_decode_fwd(const attn_decode_args_t* a, void* stream) {
     attn::CombineParams c{};
     c.part_o = part_o; c.part_lse = part_lse; c.o = a->o; c.lse = a->lse;
     c.pairs = a->batch * a->num_heads_q; c.num_splits = a->num_splits; c.o_dtype = a->o_dtype;
+    c.o_round = a->o_dtype == ATTN_BF16 ? a->o_round : 0;
 
     if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);

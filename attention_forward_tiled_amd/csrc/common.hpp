@@ -121,6 +121,23 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return Op<T>::pack(lo, hi);
 }
 
+// fp32 -> bf16 bit pattern rounded to nearest with ties away from zero (mode 1) or
+// toward zero (mode 2): add half a bf16 unit to the magnitude (mode 1) and truncate.
+// NaN stays a quiet NaN; the magnitude add cannot carry into the sign bit.
+__device__ __forceinline__ uint32_t bf16_bits_directed(float x, int mode) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return (u >> 16) | 0x0040u;
+  return ((u & 0x80000000u) | (mode == 1 ? mag + 0x8000u : mag)) >> 16;
+}
+
+// Two fp32 values -> two bf16 in one dword (lo first) with output rounding `mode`
+// (0 to nearest even, the hardware conversion; 1 ties away from zero; 2 toward zero).
+__device__ __forceinline__ uint32_t pack_bf16_round(float lo, float hi, int mode) {
+  if (mode == 0) return Op<BF16>::pack(lo, hi);
+  return bf16_bits_directed(lo, mode) | (bf16_bits_directed(hi, mode) << 16);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

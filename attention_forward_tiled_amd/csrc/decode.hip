@@ -622,7 +622,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
     const float v = o[e] * inv;
     if (p.o_dtype == kF32) static_cast<float*>(p.o)[ob + e] = v;
     else if (p.o_dtype == kF16) static_cast<uint16_t*>(p.o)[ob + e] = Op<F16>::from_float(v);
-    else static_cast<uint16_t*>(p.o)[ob + e] = Op<BF16>::from_float(v);
+    else static_cast<uint16_t*>(p.o)[ob + e] =
+        p.o_round == 0 ? Op<BF16>::from_float(v) : (uint16_t)bf16_bits_directed(v, p.o_round);
   }
   if (p.lse && lane == 0) p.lse[pair] = den > 0.f ? M + __logf(den) : -INFINITY;
 }

@@ -23,6 +23,7 @@ struct PrefillParams {
   int32_t num_blocks, max_blocks;
   int32_t bq;                   // query positions per workgroup (rows = group * bq <= 128)
   int32_t causal, o_dtype;
+  int32_t o_round;              // rounding of a bf16 output: 0 RTNE, 1 RTNA, 2 RTZ
   float scale_log2;             // softmax scale * log2(e)
   int32_t cus;                  // compute units of the device (work pairing decision)
 };
@@ -55,6 +56,7 @@ struct CombineParams {
   int32_t heads;                // H (to find the sequence of a (b, h) pair)
   int32_t max_seqlen_k;
   int32_t pairs, num_splits, o_dtype;
+  int32_t o_round;              // rounding of a bf16 output: 0 RTNE, 1 RTNA, 2 RTZ
 };
 
 // Each launcher returns hipSuccess or the launch error; shapes were validated by the caller.

@@ -394,7 +394,7 @@ void prefill_kernel(const PrefillParams p) {
               u32x2{pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3])};
         } else {
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ob + d0) =
-              u32x2{pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3])};
+              u32x2{pack_bf16_round(v[0], v[1], p.o_round), pack_bf16_round(v[2], v[3], p.o_round)};
         }
       }
     }

@@ -25,7 +25,8 @@
  *    synchronising copy): out-of-range page ids are treated as empty pages and
  *    key lengths are clamped to their stated host-side bounds, so a bad table
  *    gives wrong numbers, never an out-of-bounds access.
- *  - Outputs in fp16 / bf16 are rounded to nearest, ties to even.
+ *  - Outputs in fp16 / bf16 are rounded to nearest, ties to even, unless the call's
+ *    o_round field selects another mode for a bf16 output (attn_round_t).
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -37,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 #define ATTN_PAGE_SIZE 64      /* tokens per KV page (block_size); equal to the KV tile width */
 #define ATTN_MAX_SPLITS 64     /* upper bound of num_splits for the split-KV decode */
 
@@ -50,6 +51,13 @@ typedef enum {
 } attn_status_t;
 
 typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1, ATTN_F32 = 2 } attn_dtype_t;
+
+/* Rounding of the fp32 result to a bf16 output (page 7minutos.es / MoonMath, section
+ * "Punto de referencia", which measures all three): RTNE = to nearest, ties to even;
+ * RTNA = to nearest, ties away from zero; RTZ = toward zero (truncation). NaN stays
+ * NaN in every mode. fp16 outputs support RTNE only (ATTN_ERR_UNSUPPORTED otherwise);
+ * fp32 outputs are not rounded and accept any value of the field. */
+typedef enum { ATTN_ROUND_RTNE = 0, ATTN_ROUND_RTNA = 1, ATTN_ROUND_RTZ = 2 } attn_round_t;
 
 /* BSHD = [batch, seq, heads, d]; BHSD = [batch, heads, seq, d]. Both are accepted
  * as-is, without a transposition (page 7minutos.es / MoonMath, section
@@ -115,6 +123,7 @@ typedef struct {
   int32_t causal;
   int32_t precise;
   float scale;
+  int32_t o_round;             /* attn_round_t for a bf16 output (0 = RTNE) */
 } attn_prefill_args_t;
 
 attn_status_t attn_prefill_fwd(const attn_prefill_args_t* args, void* stream);
@@ -168,6 +177,7 @@ typedef struct {
   int32_t qkv_dtype;
   int32_t o_dtype;
   float scale;
+  int32_t o_round;             /* attn_round_t for a bf16 output (0 = RTNE) */
 } attn_decode_args_t;
 
 attn_status_t attn_decode_fwd(const attn_decode_args_t* args, void* stream);
@@ -203,6 +213,7 @@ typedef struct {
   int32_t num_splits;
   int32_t head_dim;
   int32_t o_dtype;
+  int32_t o_round;             /* attn_round_t for a bf16 output (0 = RTNE) */
 } attn_combine_args_t;
 
 attn_status_t attn_splitkv_combine(const attn_combine_args_t* args, void* stream);

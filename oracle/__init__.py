@@ -19,6 +19,8 @@ combine     the log-sum-exp merge of split-KV partial results (same page,
             section 8: partial softmax-weighted outputs combined), plus the
             per-split partials themselves.
 brute       pure-Python per-row evaluation for tiny inputs (math.exp/fsum).
+rounding    rounding to bfloat16 with ties to even, ties away from zero, or toward
+            zero (the three output modes of the MoonMath benchmark page).
 
 Parity pins: every function above is pinned by ``tests/test_oracle.py`` against
 closed forms, invariants, a library special case (torch CPU SDPA in float64)
@@ -27,3 +29,4 @@ and hand-derived golden fixtures; none is "parity unpinned".
 from .materialised import attention, attention_rows, gather_kv, kv_head_of  # noqa: F401
 from .online import online_attention_rows  # noqa: F401
 from .combine import lse_combine, split_partials  # noqa: F401
+from .rounding import round_bf16  # noqa: F401

@@ -38,7 +38,7 @@ def tolerance(case) -> float:
     return TOL_PRECISE if getattr(case, "precise", False) else TOL[case.dtype]
 
 
-def gpu_prefill(inp, *, with_lse=False, out_dtype=None):
+def gpu_prefill(inp, *, with_lse=False, out_dtype=None, out_round="rtne"):
     """Run attn_prefill_fwd on the seeded inputs; returns (O, lse) as float64 numpy."""
     from attention_forward_tiled_amd import attn_prefill_fwd
     c = inp.case
@@ -51,7 +51,7 @@ def gpu_prefill(inp, *, with_lse=False, out_dtype=None):
         lse = torch.full((c.batch, c.heads_q, c.seqlen_q), float("nan"), dtype=torch.float32, device="cuda")
     o = attn_prefill_fwd(q, k, v, causal=c.causal, block_table=bt, seqlens_k=sl,
                          seqlen_k=c.seqlen_k, layout=c.layout, out_dtype=odt, lse=lse,
-                         precise=c.precise)
+                         precise=c.precise, out_round=out_round)
     torch.cuda.synchronize()
     return to_f64(o), (to_f64(lse) if lse is not None else None)
 
@@ -71,3 +71,29 @@ def max_abs_err(a: np.ndarray, b: np.ndarray) -> float:
     if not np.isfinite(a).all():
         return float("inf")
     return float(np.abs(a - b).max()) if a.size else 0.0
+
+
+def check_bf16_rounding(o_bf16: np.ndarray, o_f32: np.ndarray, mode: str):
+    """Relations that the bf16 output of a launch must satisfy against the fp32 output
+    of the same launch (same arithmetic, only the final conversion differs): it lies
+    on the bf16 grid, within half a bf16 unit for the nearest modes and below it in
+    magnitude for RTZ; at exact ties it rounds to the even neighbour (RTNE) or away
+    from zero (RTNA)."""
+    x = o_f32.astype(np.float32)
+    r = o_bf16.astype(np.float32)
+    assert ((r.view(np.uint32) & 0xFFFF) == 0).all(), "output not on the bf16 grid"
+    xb = x.view(np.uint32)
+    nz = (xb & 0x7FFFFFFF) >= 0x00800000                      # normal fp32 values
+    ulp = np.exp2(np.floor(np.log2(np.abs(x[nz].astype(np.float64)))) - 7)
+    diff = np.abs(r[nz].astype(np.float64) - x[nz].astype(np.float64))
+    if mode == "rtz":
+        assert (np.abs(r[nz]) <= np.abs(x[nz])).all() and (diff < ulp).all()
+    else:
+        assert (diff <= ulp / 2).all()
+        tie = nz & ((xb & 0xFFFF) == 0x8000)
+        if tie.any():
+            if mode == "rtna":
+                assert (np.abs(r[tie]) > np.abs(x[tie])).all()
+            else:
+                assert ((r[tie].view(np.uint32) >> 16) & 1 == 0).all()
+    return int((nz & ((xb & 0xFFFF) == 0x8000)).sum())

@@ -41,9 +41,9 @@ def test_header_constants_match_binding():
 
 def test_struct_sizes():
     # the ctypes mirrors must have the C layout (all fields naturally aligned, no padding holes)
-    assert ctypes.sizeof(_lib.PrefillArgs) == 7 * 8 + 14 * 4
-    assert ctypes.sizeof(_lib.DecodeArgs) == 8 * 8 + 8 + 11 * 4 + 4
-    assert ctypes.sizeof(_lib.CombineArgs) == 4 * 8 + 5 * 4 + 4
+    assert ctypes.sizeof(_lib.PrefillArgs) == 7 * 8 + 15 * 4 + 4      # tail padding to 8
+    assert ctypes.sizeof(_lib.DecodeArgs) == 8 * 8 + 8 + 12 * 4
+    assert ctypes.sizeof(_lib.CombineArgs) == 4 * 8 + 6 * 4
 
 
 FAKE = 0x1000  # aligned non-null pointer value; never dereferenced (validation fails first)
@@ -53,7 +53,7 @@ def prefill_args(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, block_table=FAKE, seqlens_k=FAKE,
              batch=1, num_heads_q=4, num_heads_kv=2, seqlen_q=128, seqlen_k=128, head_dim=128,
              num_blocks=2, max_blocks_per_seq=2, qkv_dtype=_lib.ATTN_F16, o_dtype=_lib.ATTN_F16,
-             layout=_lib.ATTN_BSHD, causal=1, precise=0, scale=0.0)
+             layout=_lib.ATTN_BSHD, causal=1, precise=0, scale=0.0, o_round=_lib.ATTN_ROUND_RTNE)
     a.update(kw)
     return _lib.PrefillArgs(**a)
 
@@ -62,14 +62,14 @@ def decode_args(**kw):
     a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, block_table=FAKE, seqlens_k=FAKE, o=FAKE, lse=None,
              workspace=FAKE, workspace_bytes=1 << 30, batch=2, num_heads_q=8, num_heads_kv=2,
              head_dim=128, num_blocks=10, max_blocks_per_seq=5, max_seqlen_k=300, num_splits=4,
-             qkv_dtype=_lib.ATTN_BF16, o_dtype=_lib.ATTN_BF16, scale=0.0)
+             qkv_dtype=_lib.ATTN_BF16, o_dtype=_lib.ATTN_BF16, scale=0.0, o_round=_lib.ATTN_ROUND_RTNE)
     a.update(kw)
     return _lib.DecodeArgs(**a)
 
 
 def combine_args(**kw):
     a = dict(partial_o=FAKE, partial_lse=FAKE, o=FAKE, lse=None, batch=2, num_heads=4, num_splits=8,
-             head_dim=128, o_dtype=_lib.ATTN_F32)
+             head_dim=128, o_dtype=_lib.ATTN_F32, o_round=_lib.ATTN_ROUND_RTNE)
     a.update(kw)
     return _lib.CombineArgs(**a)
 
@@ -89,6 +89,8 @@ BAD_PREFILL = [
     (dict(scale=float("nan")), _lib.ATTN_ERR_INVALID_ARG, "scale"),
     (dict(num_heads_q=258, num_heads_kv=2), _lib.ATTN_ERR_UNSUPPORTED, "GQA"),
     (dict(batch=-1), _lib.ATTN_ERR_INVALID_ARG, "batch"),
+    (dict(o_round=3), _lib.ATTN_ERR_INVALID_ARG, "o_round"),
+    (dict(o_round=_lib.ATTN_ROUND_RTZ), _lib.ATTN_ERR_UNSUPPORTED, "fp16"),     # fp16 output
 ]
 
 
@@ -121,6 +123,8 @@ BAD_DECODE = [
     (dict(block_table=None), _lib.ATTN_ERR_INVALID_ARG, "non-NULL"),
     (dict(head_dim=32), _lib.ATTN_ERR_INVALID_ARG, "head_dim"),
     (dict(qkv_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_INVALID_ARG, "qkv_dtype"),
+    (dict(o_round=-1), _lib.ATTN_ERR_INVALID_ARG, "o_round"),
+    (dict(o_dtype=_lib.ATTN_F16, o_round=_lib.ATTN_ROUND_RTNA), _lib.ATTN_ERR_UNSUPPORTED, "fp16"),
 ]
 
 
@@ -132,7 +136,8 @@ def test_decode_rejects(lib, kw, status, msg):
 
 
 @pytest.mark.parametrize("kw,msg", [(dict(num_splits=0), "num_splits"), (dict(head_dim=100), "head_dim"),
-                                    (dict(o_dtype=3), "o_dtype"), (dict(partial_o=None), "non-NULL")])
+                                    (dict(o_dtype=3), "o_dtype"), (dict(partial_o=None), "non-NULL"),
+                                    (dict(o_round=5), "o_round")])
 def test_combine_rejects(lib, kw, msg):
     assert lib.attn_splitkv_combine(ctypes.byref(combine_args(**kw)), None) == _lib.ATTN_ERR_INVALID_ARG
     assert msg in _lib.last_error()

@@ -6,20 +6,21 @@ import torch
 
 import oracle
 from attn_workloads import CONFIGS, DecodeCase, bits_to_f64, make_decode_inputs
-from gpu_util import TOL, dev, dev_i32, max_abs_err, say, to_f64
+from gpu_util import TOL, check_bf16_rounding, dev, dev_i32, max_abs_err, say, to_f64
+from oracle.rounding import round_bf16
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def gpu_decode(inp, num_splits, out_dtype=None, with_lse=False):
+def gpu_decode(inp, num_splits, out_dtype=None, with_lse=False, out_round="rtne"):
     from attention_forward_tiled_amd import attn_decode_fwd
     c = inp.case
     lse = torch.full((c.batch, c.heads_q), float("nan"), device="cuda") if with_lse else None
     o = attn_decode_fwd(dev(inp.q, c.dtype), dev(inp.k_cache, c.dtype), dev(inp.v_cache, c.dtype),
                         dev_i32(inp.block_table), dev_i32(inp.seqlens_k),
                         max_seqlen_k=inp.max_seqlen_k, num_splits=num_splits,
-                        out_dtype=out_dtype, lse=lse)
+                        out_dtype=out_dtype, lse=lse, out_round=out_round)
     torch.cuda.synchronize()
     return to_f64(o), (to_f64(lse) if with_lse else None)
 
@@ -161,3 +162,30 @@ def test_combine_against_formula(d, odt):
     assert np.isneginf(L[0, 0]) and np.isneginf(lref[0, 0])
     fin = np.isfinite(lref)
     assert np.abs(L[fin] - lref[fin]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("mode", ["rtne", "rtna", "rtz"])
+def test_decode_bf16_output_rounding(mode):
+    case = DecodeCase("bf16_round_dec", 4, 16, 4, 128, "bf16", lengths_fixed=(900, 64, 3000, 17))
+    inp = make_decode_inputs(case, seed=12)
+    say(f"decode bf16 output rounding {mode}")
+    O, _ = gpu_decode(inp, 8, out_round=mode)
+    O32, _ = gpu_decode(inp, 8, out_dtype=torch.float32)
+    Oref, _ = oracle_decode(inp)
+    assert max_abs_err(O, round_bf16(Oref, mode)) <= TOL[case.dtype]
+    check_bf16_rounding(O, O32, mode)
+
+
+@pytest.mark.parametrize("mode", ["rtna", "rtz"])
+def test_combine_bf16_output_rounding(mode):
+    from attention_forward_tiled_amd import attn_splitkv_combine
+    say(f"combine bf16 output rounding {mode}")
+    po, pl = _partials(77, d=128)
+    a = torch.from_numpy(po).cuda()
+    b = torch.from_numpy(pl).cuda()
+    o = attn_splitkv_combine(a, b, out_dtype=torch.bfloat16, out_round=mode)
+    o32 = attn_splitkv_combine(a, b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Oref, _ = oracle.lse_combine(po.astype(np.float64), pl.astype(np.float64))
+    assert max_abs_err(to_f64(o), round_bf16(Oref, mode)) <= 4e-2
+    check_bf16_rounding(to_f64(o), to_f64(o32), mode)

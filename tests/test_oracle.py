@@ -446,3 +446,78 @@ def test_plant_combine_without_weights(monkeypatch):
         return O, partial_lse.max(axis=-1)
     monkeypatch.setattr(ocomb, "lse_combine", plain_mean)
     assert _fails(check_split_combine)
+
+
+# ---------------------------------------------------------------- bfloat16 output rounding
+# The benchmark page measures bf16 outputs in three rounding modes: to nearest with ties
+# to even (RTNE), to nearest with ties away from zero (RTNA), toward zero (RTZ). Pins:
+# hand-derived values, the library's own RTNE conversion (torch float32 -> bfloat16),
+# and bit-level formulations on float32 patterns that share nothing with the oracle's
+# exact arithmetic.
+
+from oracle.rounding import round_bf16, round_bf16_scalar  # noqa: E402
+
+# (x, RTNE, RTNA, RTZ); bfloat16 keeps 7 fraction bits: next value after 1 is 1 + 2^-7.
+ROUND_CASES = [
+    (1.0, 1.0, 1.0, 1.0),
+    (1 + 2 ** -8, 1.0, 1 + 2 ** -7, 1.0),                      # exact tie, even neighbour is 1
+    (1 + 3 * 2 ** -8, 1 + 2 * 2 ** -7, 1 + 2 * 2 ** -7, 1 + 2 ** -7),   # tie, even neighbour is above
+    (-(1 + 2 ** -8), -1.0, -(1 + 2 ** -7), -1.0),              # sign-symmetric
+    (1 + 2 ** -9, 1.0, 1.0, 1.0),                              # below the tie
+    (1 + 2 ** -8 + 2 ** -20, 1 + 2 ** -7, 1 + 2 ** -7, 1.0),  # just above the tie
+    (3.4e38, math.inf, math.inf, (2 - 2 ** -7) * 2 ** 127),    # overflow: RTZ stays finite
+    (-(2 ** -134), -0.0, -(2 ** -133), -0.0),                  # half the smallest subnormal
+    (2.5 * 2 ** -133, 2 * 2 ** -133, 3 * 2 ** -133, 2 * 2 ** -133),   # subnormal tie
+]
+
+
+@pytest.mark.parametrize("x,rtne,rtna,rtz", ROUND_CASES)
+def test_round_bf16_hand_values(x, rtne, rtna, rtz):
+    for mode, want in (("rtne", rtne), ("rtna", rtna), ("rtz", rtz)):
+        got = round_bf16_scalar(x, mode)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (x, mode, got, want)
+
+
+def _random_f32(n, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
+    x[::7] = (x[::7].view(np.uint32) & 0xFFFF0000 | (1 << 15)).view(np.float32)   # exact ties
+    return x
+
+
+def test_round_bf16_rtne_matches_torch():
+    x = _random_f32(4000, 1)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_bf16(x.astype(np.float64), "rtne"), want)
+
+
+def test_round_bf16_bit_formulations():
+    x = _random_f32(4000, 2)
+    bits = x.view(np.uint32).astype(np.uint64)
+    sign = bits & 0x80000000
+    mag = bits & 0x7FFFFFFF
+    rtz = (sign | (mag & 0x7FFF0000)).astype(np.uint32).view(np.float32).astype(np.float64)
+    rtna = (sign | ((mag + 0x8000) & 0x7FFF0000)).astype(np.uint32).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(round_bf16(x.astype(np.float64), "rtz"), rtz)
+    np.testing.assert_array_equal(round_bf16(x.astype(np.float64), "rtna"), rtna)
+
+
+def test_round_bf16_properties():
+    x = _random_f32(2000, 3).astype(np.float64)
+    for mode in ("rtne", "rtna", "rtz"):
+        r = round_bf16(x, mode)
+        assert (r.astype(np.float32).view(np.uint32) & 0xFFFF).max() == 0     # on the bf16 grid
+        ulp = np.exp2(np.floor(np.log2(np.abs(x))) - 7)
+        if mode == "rtz":
+            assert (np.abs(r) <= np.abs(x)).all() and (np.abs(x) - np.abs(r) < ulp).all()
+        else:
+            assert (np.abs(r - x) <= ulp / 2).all()
+
+
+def test_round_bf16_keeps_shape_and_order():
+    # a transposed (non-contiguous) view, as attention outputs in BSHD are
+    x = _random_f32(2 * 3 * 5, 4).astype(np.float64).reshape(2, 3, 5).transpose(0, 2, 1)
+    r = round_bf16(x, "rtz")
+    assert r.shape == x.shape
+    for idx in np.ndindex(*x.shape):
+        assert r[idx] == round_bf16_scalar(float(x[idx]), "rtz")

@@ -11,7 +11,8 @@ import pytest
 import torch
 
 from attn_workloads import CONFIGS, PrefillCase, make_prefill_inputs
-from gpu_util import gpu_prefill, max_abs_err, oracle_prefill, say, tolerance
+from gpu_util import check_bf16_rounding, gpu_prefill, max_abs_err, oracle_prefill, say, tolerance
+from oracle.rounding import round_bf16
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -162,3 +163,19 @@ def test_prefill_one_group_sampled(case):
     err = max_abs_err(O[:, rows], Oref)
     say(f"  max abs err {err:.3e} over {rows.size} rows x all (b, h)")
     assert err <= tolerance(case)
+
+
+@pytest.mark.parametrize("mode", ["rtne", "rtna", "rtz"])
+def test_prefill_bf16_output_rounding(mode):
+    # the three bf16 output modes of the MoonMath benchmark page: parity against the
+    # oracle rounded in the same mode, and the rounding relations against the fp32
+    # output of the same launch
+    case = P("bf16_round", 2, 8, 2, 160, 300, 128, "bf16", True, "paged")
+    say(f"prefill bf16 output rounding {mode}")
+    inp = make_prefill_inputs(case, seed=11)
+    O, _ = gpu_prefill(inp, out_round=mode)
+    O32, _ = gpu_prefill(inp, out_dtype="f32")
+    Oref, _ = oracle_prefill(inp)
+    assert max_abs_err(O, round_bf16(Oref, mode)) <= tolerance(case)
+    ties = check_bf16_rounding(O, O32, mode)
+    say(f"  {ties} exact ties among {O.size} outputs")
