@@ -18,7 +18,7 @@ ATTN_BSHD, ATTN_BHSD = 0, 1
 ATTN_ROUND_RTNE, ATTN_ROUND_RTNA, ATTN_ROUND_RTZ = 0, 1, 2
 ATTN_PAGE_SIZE = 64
 ATTN_MAX_SPLITS = 64
-ATTN_ABI_VERSION = 2
+ATTN_ABI_VERSION = 3
 
 EXPORTS = ("attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes",
            "attn_splitkv_combine", "attn_last_error", "attn_abi_version", "attn_device_count")
@@ -29,6 +29,7 @@ _c_void_p, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 class PrefillArgs(ctypes.Structure):
     _fields_ = [("q", _c_void_p), ("k", _c_void_p), ("v", _c_void_p), ("o", _c_void_p),
                 ("lse", _c_void_p), ("block_table", _c_void_p), ("seqlens_k", _c_void_p),
+                ("cu_seqlens_q", _c_void_p),
                 ("batch", _i32), ("num_heads_q", _i32), ("num_heads_kv", _i32),
                 ("seqlen_q", _i32), ("seqlen_k", _i32), ("head_dim", _i32),
                 ("num_blocks", _i32), ("max_blocks_per_seq", _i32),

@@ -61,21 +61,33 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
                      layout: str = "bshd", out: Optional[torch.Tensor] = None,
                      out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
                      scale: float = 0.0, precise: bool = False, out_round: str = "rtne",
+                     cu_seqlens_q: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
                      stream=None) -> torch.Tensor:
     """Tiled attention forward. q: [B,S_q,Hq,d] (bshd) or [B,Hq,S_q,d] (bhsd).
 
     Paged K/V (block_table given): k, v are [num_blocks, 64, Hkv, d] caches and
     seqlens_k [B] int32 is required; ``seqlen_k`` (host-side bound) defaults to
     64 * block_table.shape[1]. Dense K/V: k, v in the layout of q.
+
+    Packed queries: with ``cu_seqlens_q`` ([B+1] int32, first row of each sequence)
+    q and the output are [total_q, Hq, d] and ``max_seqlen_q`` bounds the per-sequence
+    query counts; lse, when given, is [Hq, total_q].
     """
     _need(q, "q", (torch.float16, torch.bfloat16))
     _need(k, "k", (q.dtype,))
     _need(v, "v", (q.dtype,))
     if layout not in _LAYOUT:
         raise ValueError("layout must be 'bshd' or 'bhsd'")
-    if q.dim() != 4:
+    if cu_seqlens_q is not None:
+        _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,))
+        if q.dim() != 3 or layout != "bshd":
+            raise ValueError("packed queries: q must be [total_q, Hq, d] (bshd)")
+        if max_seqlen_q is None:
+            raise ValueError("packed queries need max_seqlen_q")
+        B, (_, Hq, d), Sq = cu_seqlens_q.numel() - 1, q.shape, int(max_seqlen_q)
+    elif q.dim() != 4:
         raise ValueError("q must be 4-D")
-    if layout == "bshd":
+    elif layout == "bshd":
         B, Sq, Hq, d = q.shape
     else:
         B, Hq, Sq, d = q.shape
@@ -102,11 +114,16 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     _need(out, "out", tuple(_DT))
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
     if lse is not None:
         _need(lse, "lse", (torch.float32,))
+        want = (Hq, q.shape[0]) if cu_seqlens_q is not None else (B, Hq, Sq)
+        if tuple(lse.shape) != want:
+            raise ValueError(f"lse must be {list(want)}")
     a = _lib.PrefillArgs(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(block_table), _ptr(seqlens_k),
-        B, Hq, Hkv, Sq, Sk, d, num_blocks, max_blocks, _DT[q.dtype], _DT[out.dtype],
+        _ptr(cu_seqlens_q), B, Hq, Hkv, Sq, Sk, d, num_blocks, max_blocks, _DT[q.dtype], _DT[out.dtype],
         _LAYOUT[layout], int(bool(causal)), int(bool(precise)), float(scale), _round(out_round))
     _check(_lib.load().attn_prefill_fwd(ctypes.byref(a), _stream(stream)))
     return out

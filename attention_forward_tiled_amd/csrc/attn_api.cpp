@@ -134,6 +134,10 @@ attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
       if (!aligned4(a->block_table)) return fail(ATTN_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
     }
     if (a->seqlens_k && !aligned4(a->seqlens_k)) return fail(ATTN_ERR_INVALID_ARG, "seqlens_k must be 4-byte aligned");
+    if (a->cu_seqlens_q) {
+      if (a->layout != ATTN_BSHD) return fail(ATTN_ERR_INVALID_ARG, "packed queries (cu_seqlens_q) need the BSHD layout");
+      if (!aligned4(a->cu_seqlens_q)) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q must be 4-byte aligned");
+    }
     if (a->batch == 0 || a->seqlen_q == 0) return ok();
     if (!a->q || !a->k || !a->v || !a->o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
@@ -157,7 +161,9 @@ attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
       p.q_sb = Hq * Sq * D; p.q_sh = Sq * D; p.q_ss = D;
       p.kv_sb = Hkv * Sk * D; p.kv_sh = Sk * D; p.kv_ss = D;
     }
+    if (a->cu_seqlens_q) p.q_sb = 0;   // packed: rows of every sequence in one [total_q, Hq, d]
     p.o_sb = p.q_sb; p.o_sh = p.q_sh; p.o_ss = p.q_ss;
+    p.cu_seqlens_q = a->cu_seqlens_q;
     p.batch = a->batch; p.hq = a->num_heads_q; p.hkv = a->num_heads_kv; p.group = G;
     p.seqlen_q = a->seqlen_q; p.seqlen_k = a->seqlen_k;
     p.num_blocks = a->num_blocks; p.max_blocks = a->max_blocks_per_seq;

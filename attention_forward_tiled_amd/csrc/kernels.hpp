@@ -16,6 +16,7 @@ struct PrefillParams {
   float* lse;
   const int32_t* block_table;   // null for dense K/V
   const int32_t* seqlens_k;     // null: every sequence has seqlen_k keys
+  const int32_t* cu_seqlens_q;  // null, or [B + 1] first packed query row of each sequence
   int64_t q_sb, q_sh, q_ss;     // element strides of Q over (batch, head, position)
   int64_t o_sb, o_sh, o_ss;     // same for O (elements of o_dtype)
   int64_t kv_sb, kv_sh, kv_ss;  // dense K/V strides over (batch, kv head, position)

@@ -105,7 +105,16 @@ void prefill_kernel(const PrefillParams p) {
 
   int L = p.seqlen_k;
   if (p.seqlens_k) L = min(max(scalar_load(p.seqlens_k + b), 0), p.seqlen_k);
-  const int off = L - p.seqlen_q;       // bottom-right alignment of the causal mask
+  // Queries of this sequence: S_q rows from row qrow0 (packed queries: the sequence's
+  // own count and first row in the shared buffer).
+  int sq = p.seqlen_q;
+  int64_t qrow0 = 0;
+  if (p.cu_seqlens_q) {
+    const int c0 = scalar_load(p.cu_seqlens_q + b);
+    sq = min(max(scalar_load(p.cu_seqlens_q + b + 1) - c0, 0), p.seqlen_q);
+    qrow0 = c0;
+  }
+  const int off = L - sq;               // bottom-right alignment of the causal mask
   const float c = p.scale_log2;
 
   // state of the current query block (set at the start of each item)
@@ -315,8 +324,8 @@ void prefill_kernel(const PrefillParams p) {
       const int hig = r / p.bq;
       rpos = q0 + (r - hig * p.bq);
       rh = kvh * p.group + hig;
-      rok = hig < p.group && rpos < p.seqlen_q;
-      const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (int64_t)rpos * p.q_ss;
+      rok = hig < p.group && rpos < sq;
+      const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (qrow0 + rpos) * p.q_ss;
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = rok ? ldg16(qp + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
     }
@@ -324,9 +333,9 @@ void prefill_kernel(const PrefillParams p) {
     // ---- tile range: [0, n_full) need no masking, [n_full, n_tiles) straddle a boundary;
     // group g takes tiles [g*h, min((g+1)*h, n_tiles)), h = ceil(n_tiles / NG)
     {
-      const int pmax = min(q0 + p.bq, p.seqlen_q) - 1;
+      const int pmax = min(q0 + p.bq, sq) - 1;
       const int kv_end = p.causal ? min(L, pmax + off + 1) : L;
-      const int n_tiles = kv_end > 0 ? (kv_end + kPage - 1) / kPage : 0;
+      const int n_tiles = kv_end > 0 && q0 < sq ? (kv_end + kPage - 1) / kPage : 0;
       n_full = L / kPage;
       if (p.causal) n_full = min(n_full, max(q0 + off + 1, 0) / kPage);
       n_full = min(n_full, n_tiles);
@@ -380,7 +389,7 @@ void prefill_kernel(const PrefillParams p) {
     const float l = wave_sum_xor(lsum, 32);
     if (grp == 0 && rok) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (int64_t)rpos * p.o_ss;
+    const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (qrow0 + rpos) * p.o_ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -398,8 +407,12 @@ void prefill_kernel(const PrefillParams p) {
         }
       }
     }
-    if (p.lse && half == 0)
-      p.lse[((int64_t)b * p.hq + rh) * p.seqlen_q + rpos] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+    if (p.lse && half == 0) {
+      // [B, Hq, S_q], or [Hq, total_q] for packed queries
+      const int64_t li = p.cu_seqlens_q ? (int64_t)rh * scalar_load(p.cu_seqlens_q + p.batch) + qrow0 + rpos
+                                        : ((int64_t)b * p.hq + rh) * p.seqlen_q + rpos;
+      p.lse[li] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+    }
     }
     if constexpr (PAIR) __syncthreads();   // the LDS of this item is the next item's staging area
   }

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 #define ATTN_PAGE_SIZE 64      /* tokens per KV page (block_size); equal to the KV tile width */
 #define ATTN_MAX_SPLITS 64     /* upper bound of num_splits for the split-KV decode */
 
@@ -96,10 +96,22 @@ typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
  *  causal   0 or 1. precise: 0 or 1; 1 keeps the probabilities P at ~fp32 precision
  *           in the P.V product (two fp16/bf16 MFMA terms, hi + lo), for an fp32 O.
  *  scale    softmax scale; 0 selects 1/sqrt(d).
+ *  o_round  attn_round_t for a bf16 output.
+ *
+ * Packed queries (cu_seqlens_q != NULL, BSHD only): sequences of different query
+ * counts share one buffer. q and o are [total_q, Hq, d]; int32 cu_seqlens_q [B + 1]
+ * (device) holds the first row of every sequence, cu_seqlens_q[B] = total_q, so
+ * sequence b has S_q,b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] queries (clamped to
+ * [0, seqlen_q]; seqlen_q is then the host-side maximum). The operation above holds
+ * per sequence with S_q,b in place of S_q, including the bottom-right causal offset
+ * L_b - S_q,b (a batch of chunked-prefill steps of different lengths). lse, when
+ * given, is fp32 [Hq, total_q]. The caller sizes q, o and lse for total_q; the
+ * library reads cu_seqlens_q only on the device.
  * Errors: INVALID_ARG for null required pointers, misalignment, non-positive
  * sizes (B or S_q of 0 is a no-op returning OK), d not in {64,128,256}, a head
  * count that is not a multiple, a paged cache whose table cannot hold seqlen_k
- * keys (64*max_blocks_per_seq < seqlen_k), bad enum values.
+ * keys (64*max_blocks_per_seq < seqlen_k), bad enum values, packed queries with the
+ * BHSD layout or a misaligned cu_seqlens_q.
  */
 typedef struct {
   const void* q;
@@ -109,6 +121,7 @@ typedef struct {
   float* lse;
   const int32_t* block_table;
   const int32_t* seqlens_k;
+  const int32_t* cu_seqlens_q; /* NULL, or packed queries: see "Packed queries" */
   int32_t batch;
   int32_t num_heads_q;
   int32_t num_heads_kv;

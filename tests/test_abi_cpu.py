@@ -41,7 +41,7 @@ def test_header_constants_match_binding():
 
 def test_struct_sizes():
     # the ctypes mirrors must have the C layout (all fields naturally aligned, no padding holes)
-    assert ctypes.sizeof(_lib.PrefillArgs) == 7 * 8 + 15 * 4 + 4      # tail padding to 8
+    assert ctypes.sizeof(_lib.PrefillArgs) == 8 * 8 + 15 * 4 + 4      # tail padding to 8
     assert ctypes.sizeof(_lib.DecodeArgs) == 8 * 8 + 8 + 12 * 4
     assert ctypes.sizeof(_lib.CombineArgs) == 4 * 8 + 6 * 4
 
@@ -50,7 +50,7 @@ FAKE = 0x1000  # aligned non-null pointer value; never dereferenced (validation 
 
 
 def prefill_args(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, block_table=FAKE, seqlens_k=FAKE,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, block_table=FAKE, seqlens_k=FAKE, cu_seqlens_q=None,
              batch=1, num_heads_q=4, num_heads_kv=2, seqlen_q=128, seqlen_k=128, head_dim=128,
              num_blocks=2, max_blocks_per_seq=2, qkv_dtype=_lib.ATTN_F16, o_dtype=_lib.ATTN_F16,
              layout=_lib.ATTN_BSHD, causal=1, precise=0, scale=0.0, o_round=_lib.ATTN_ROUND_RTNE)
@@ -91,6 +91,8 @@ BAD_PREFILL = [
     (dict(batch=-1), _lib.ATTN_ERR_INVALID_ARG, "batch"),
     (dict(o_round=3), _lib.ATTN_ERR_INVALID_ARG, "o_round"),
     (dict(o_round=_lib.ATTN_ROUND_RTZ), _lib.ATTN_ERR_UNSUPPORTED, "fp16"),     # fp16 output
+    (dict(cu_seqlens_q=FAKE, layout=_lib.ATTN_BHSD), _lib.ATTN_ERR_INVALID_ARG, "BSHD"),
+    (dict(cu_seqlens_q=FAKE + 2), _lib.ATTN_ERR_INVALID_ARG, "cu_seqlens_q"),
 ]
 
 

@@ -10,8 +10,10 @@ import numpy as np
 import pytest
 import torch
 
-from attn_workloads import CONFIGS, PrefillCase, make_prefill_inputs
-from gpu_util import check_bf16_rounding, gpu_prefill, max_abs_err, oracle_prefill, say, tolerance
+import oracle
+from attn_workloads import CONFIGS, PrefillCase, bits_to_f64, make_prefill_inputs
+from gpu_util import (check_bf16_rounding, dev, dev_i32, gpu_prefill, max_abs_err, oracle_prefill, say,
+                      to_f64, tolerance)
 from oracle.rounding import round_bf16
 
 pytestmark = [pytest.mark.gpu,
@@ -179,3 +181,53 @@ def test_prefill_bf16_output_rounding(mode):
     assert max_abs_err(O, round_bf16(Oref, mode)) <= tolerance(case)
     ties = check_bf16_rounding(O, O32, mode)
     say(f"  {ties} exact ties among {O.size} outputs")
+
+
+# Packed queries: sequences with their own query counts in one [total_q, Hq, d] buffer
+# (cu_seqlens_q), each with the bottom-right causal offset L_b - S_q,b. The oracle runs
+# sequence by sequence on the same seeded values (drawn padded to the longest sequence).
+VARLEN = [
+    (P("f16_d128_causal_paged_varlen", 4, 8, 2, 257, 1000, 128, "f16", True, "paged",
+       seqlens_k=(300, 50, 200, 1000)), (100, 0, 257, 64)),
+    (P("bf16_d64_noncausal_dense_varlen", 3, 4, 4, 200, 130, 64, "bf16", False, "dense",
+       seqlens_k=(130, 7, 130)), (33, 200, 1)),
+    (P("bf16_d128_causal_paged_gqa4_varlen", 3, 16, 4, 700, 900, 128, "bf16", True, "paged",
+       seqlens_k=(900, 700, 333)), (700, 129, 333)),
+]
+
+
+@pytest.mark.parametrize("case,q_lens", VARLEN, ids=lambda x: getattr(x, "name", str(x)))
+def test_prefill_packed_queries(case, q_lens):
+    from attention_forward_tiled_amd import attn_prefill_fwd
+    say(f"prefill parity, packed queries {case.name} q_lens={q_lens}")
+    inp = make_prefill_inputs(case, seed=13)
+    c = case
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q_packed = np.concatenate([inp.q[b, :n] for b, n in enumerate(q_lens)], axis=0)   # [total, Hq, d]
+    q = dev(q_packed, c.dtype)
+    k, v = dev(inp.k, c.dtype), dev(inp.v, c.dtype)
+    bt = dev_i32(inp.block_table) if inp.block_table is not None else None
+    lse = torch.full((c.heads_q, int(cu[-1])), float("nan"), dtype=torch.float32, device="cuda")
+    o = attn_prefill_fwd(q, k, v, causal=c.causal, block_table=bt, seqlens_k=dev_i32(inp.seqlens_k),
+                         seqlen_k=c.seqlen_k, cu_seqlens_q=dev_i32(cu), max_seqlen_q=c.seqlen_q, lse=lse)
+    torch.cuda.synchronize()
+    O, L = to_f64(o), to_f64(lse)
+    qf = bits_to_f64(inp.q, c.dtype)
+    kf, vf = bits_to_f64(inp.k, c.dtype), bits_to_f64(inp.v, c.dtype)
+    for b, n in enumerate(q_lens):
+        if n == 0:
+            continue
+        if inp.block_table is not None:
+            Oref, lref = oracle.attention(qf[b:b + 1, :n], kf, vf, causal=c.causal,
+                                          block_table=inp.block_table[b:b + 1], seqlens_k=inp.seqlens_k[b:b + 1])
+        else:
+            Oref, lref = oracle.attention(qf[b:b + 1, :n], kf[b:b + 1], vf[b:b + 1], causal=c.causal,
+                                          seqlens_k=inp.seqlens_k[b:b + 1])
+        rows = slice(int(cu[b]), int(cu[b + 1]))
+        err = max_abs_err(O[rows], Oref[0])
+        say(f"  sequence {b}: {n} queries, {int(inp.seqlens_k[b])} keys, max abs err {err:.3e}")
+        assert err <= tolerance(case)
+        lg, lr = L[:, rows], lref[0]
+        fin = np.isfinite(lr)
+        assert (np.isneginf(lg) == np.isneginf(lr)).all()
+        assert np.abs(lg[fin] - lr[fin]).max(initial=0.0) <= lse_tolerance(case)
