@@ -65,6 +65,28 @@ def oracle_prefill(inp, q_index=None):
                             seqlens_k=inp.seqlens_k, q_index=q_index)
 
 
+def oracle_decode(inp, seqs=None):
+    """fp64 oracle on the chosen sequences only (their pages copied out of the pool)."""
+    c = inp.case
+    seqs = list(range(c.batch)) if seqs is None else list(seqs)
+    tables, pages = [], []
+    for b in seqs:
+        n = -(-int(inp.seqlens_k[b]) // 64)
+        tables.append(list(range(len(pages), len(pages) + n)))
+        pages.extend(int(x) for x in inp.block_table[b, :n])
+    width = max(1, max(len(t) for t in tables))
+    table = np.zeros((len(seqs), width), dtype=np.int64)
+    for i, t in enumerate(tables):
+        table[i, :len(t)] = t
+    pages = pages or [0]
+    k = bits_to_f64(inp.k_cache[pages], c.dtype)
+    v = bits_to_f64(inp.v_cache[pages], c.dtype)
+    q = bits_to_f64(inp.q[seqs], c.dtype)                      # [n, 1, Hq, d]
+    O, lse = oracle.attention(q, k, v, causal=False, block_table=table,
+                              seqlens_k=inp.seqlens_k[seqs])
+    return O[:, 0], lse[:, :, 0]
+
+
 def max_abs_err(a: np.ndarray, b: np.ndarray) -> float:
     if a.shape != b.shape:
         raise AssertionError(f"shape mismatch {a.shape} vs {b.shape}")

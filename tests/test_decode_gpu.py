@@ -5,8 +5,8 @@ import pytest
 import torch
 
 import oracle
-from attn_workloads import CONFIGS, DecodeCase, bits_to_f64, make_decode_inputs
-from gpu_util import TOL, check_bf16_rounding, dev, dev_i32, max_abs_err, say, to_f64
+from attn_workloads import CONFIGS, DecodeCase, make_decode_inputs
+from gpu_util import TOL, check_bf16_rounding, dev, dev_i32, max_abs_err, oracle_decode, say, to_f64
 from oracle.rounding import round_bf16
 
 pytestmark = [pytest.mark.gpu,
@@ -25,26 +25,6 @@ def gpu_decode(inp, num_splits, out_dtype=None, with_lse=False, out_round="rtne"
     return to_f64(o), (to_f64(lse) if with_lse else None)
 
 
-def oracle_decode(inp, seqs=None):
-    """fp64 oracle on the chosen sequences only (their pages copied out of the pool)."""
-    c = inp.case
-    seqs = list(range(c.batch)) if seqs is None else list(seqs)
-    tables, pages = [], []
-    for b in seqs:
-        n = -(-int(inp.seqlens_k[b]) // 64)
-        tables.append(list(range(len(pages), len(pages) + n)))
-        pages.extend(int(x) for x in inp.block_table[b, :n])
-    width = max(1, max(len(t) for t in tables))
-    table = np.zeros((len(seqs), width), dtype=np.int64)
-    for i, t in enumerate(tables):
-        table[i, :len(t)] = t
-    pages = pages or [0]
-    k = bits_to_f64(inp.k_cache[pages], c.dtype)
-    v = bits_to_f64(inp.v_cache[pages], c.dtype)
-    q = bits_to_f64(inp.q[seqs], c.dtype)                      # [n, 1, Hq, d]
-    O, lse = oracle.attention(q, k, v, causal=False, block_table=table,
-                              seqlens_k=inp.seqlens_k[seqs])
-    return O[:, 0], lse[:, :, 0]
 
 
 SMALL = [
