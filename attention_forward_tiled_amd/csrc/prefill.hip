@@ -29,7 +29,8 @@
 //     masks scores and fetches rows past the key length from a block of zeros (NaN in
 //     unused page slots never meets a zero probability in P.V).
 //   * The reference maximum behind o and l moves lazily: only when a row's maximum
-//     exceeds it by more than 2^8, so the O rescale is skipped on most tiles.
+//     exceeds it by more than 2^8, so the O rescale is skipped on most tiles; each lane
+//     tests its own scores first, so most tiles also skip the cross-lane max exchange.
 //   * Row sums of P are taken from the packed 16-bit P with v_dot2 (the same values
 //     the P.V MFMA consumes).
 //   * The workgroup order is reversed over query blocks so that, under a causal
@@ -219,19 +220,24 @@ void prefill_kernel(const PrefillParams p) {
           sc[kb][e] = vis ? sc[kb][e] : -INFINITY;
         }
     }
-    float mx = sc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (kb | e) mx = fmaxf(mx, sc[kb][e]);
-    const float mt = wave_max_xor(mx, 32) * c;
 
-    // online softmax with a lazily moved reference maximum: o and l are kept relative to
+    // Online softmax with a lazily moved reference maximum: o and l are kept relative to
     // mref, which only moves (rescaling o and l by 2^(old - new)) when the row maximum
-    // exceeds it by more than kLazy, so every p stays <= 2^kLazy.
-    const bool up = mt > mref + kLazy;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    // exceeds it by more than kLazy, so every p stays <= 2^kLazy. A lane first checks its
+    // own 32 scores (a shallow max tree, no cross-lane exchange); only when some lane sees
+    // a score above the slack is the row maximum formed across the two lanes of each row.
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float16v& x = sc[i >> 2];
+      const int e = 4 * (i & 3);
+      m8[i] = fmaxf(fmaxf(x[e], x[e + 1]), fmaxf(x[e + 2], x[e + 3]));
+    }
+    const float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                           fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    if (__builtin_amdgcn_ballot_w64(mx * c > mref + kLazy) != 0) {
+      const float mt = wave_max_xor(mx, 32) * c;
+      const bool up = mt > mref + kLazy;
       const float nref = up ? mt : mref;
       const float alpha = up ? fast_exp2(mref - nref) : 1.f;
       mref = nref;
