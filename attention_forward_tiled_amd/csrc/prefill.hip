@@ -45,8 +45,6 @@ namespace attn {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kLazy = 8.0f;          // log2-domain slack before the reference max moves
 
 // 16-byte chunk swizzle, chunk' = chunk ^ swz(row). It must spread two read patterns
@@ -67,25 +65,28 @@ __device__ __forceinline__ int swz(int row) {
   }
 }
 
-// NG groups of four waves per workgroup. With NG = 2 both groups own the same 128 query
-// rows and split the workgroup's key tiles between them, merging their (o, m, l) at the
-// end; this halves the longest workgroup when there are too few workgroups to balance
-// the causal triangle. Each group has its own two LDS stages. With PAIR, a workgroup
+// NG groups of NW waves per workgroup; a group owns 32 * NW query rows. With NG = 2 (NW = 4)
+// both groups own the same 128 query rows and split the workgroup's key tiles between
+// them, merging their (o, m, l) at the end; this halves the longest workgroup when there
+// are too few workgroups to balance the causal triangle. Each group has its own two LDS
+// stages. With NW = 8 (NG = 1) eight waves share every K/V tile copied to LDS, which
+// halves the copy traffic per query row on large launches. With PAIR, a workgroup
 // processes two query blocks of one (sequence, KV head) in turn (see below).
-template <int D, int NG, typename T, bool PRECISE, bool PAIR>
-__global__ __launch_bounds__(kThreads * NG, D == 256 ? 1 : 2)
+template <int D, int NG, int NW, typename T, bool PRECISE, bool PAIR>
+__global__ __launch_bounds__(64 * NW * NG, D == 256 ? 1 : 2)
 void prefill_kernel(const PrefillParams p) {
   constexpr int KS = D / 16;            // k-steps (16 deep) of the S^T product
   constexpr int DB = D / 32;            // 32-wide d blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 512 / D;          // rows covered by one 1 KiB wave-wide LDS copy
-  constexpr int NIW = kPage / RPI / kWaves;   // such copies per wave per tile (K and V each)
+  constexpr int NIW = kPage / RPI / NW;   // such copies per wave per tile (K and V each)
   constexpr int TILE = kPage * D;       // elements per K (or V) tile
   constexpr int ROWB = D * 2;           // bytes per LDS row
   __shared__ __align__(16) uint16_t smem[NG * 2 * 2 * TILE];   // [group][2 stages][K, V][TILE]
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int grp = tid >> 8, wave = (tid >> 6) & 3;   // key-range group, wave inside the group
+  const int grp = tid / (64 * NW);                              // key-range group
+  const int wave = (tid >> 6) % NW;                            // wave inside it
   const int lq = lane & 31, half = lane >> 5;        // query column, k-half of the 32x32 layouts
 
   // The dispatcher hands workgroups to the 8 XCDs round-robin. Workgroup x is given work
@@ -142,7 +143,9 @@ void prefill_kernel(const PrefillParams p) {
     int64_t base;
     bool page_ok = true;
     if (paged) {
-      const int pg = scalar_load(p.block_table + (int64_t)b * p.max_blocks + j);
+      // j is wave-uniform: say so, so that the page id comes in by a scalar load, which
+      // leaves the vector-memory counter to the tile copies
+      const int pg = scalar_load(p.block_table + (int64_t)b * p.max_blocks + __builtin_amdgcn_readfirstlane(j));
       page_ok = pg >= 0 && pg < p.num_blocks;
       base = (int64_t)(page_ok ? pg : 0) * kPage * p.hkv * D + (int64_t)kvh * D;
     } else {
@@ -301,8 +304,6 @@ void prefill_kernel(const PrefillParams p) {
     }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
   using Full = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
 
@@ -357,8 +358,8 @@ void prefill_kernel(const PrefillParams p) {
 
     if (j0 < j1) issue_tile(j0, 0);
     for (int i = 0; i < h; i += 2) {
-      step(i, S0{});
-      if (i + 1 < h) step(i + 1, S1{});
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < h) step(i + 1, std::integral_constant<int, 1>{});
     }
 
     if constexpr (NG == 2) {
@@ -431,15 +432,27 @@ void prefill_kernel(const PrefillParams p) {
 // step is about 10% cheaper.)
 constexpr int64_t kSplitBelow = 2048;
 
-template <int D, int NG, typename T, bool PRECISE, bool PAIR = false>
+template <int D, int NG, int NW, typename T, bool PRECISE, bool PAIR = false>
 hipError_t launch_ng(const PrefillParams& p, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, NG, T, PRECISE, PAIR>), dim3((unsigned)blocks),
-                     dim3(kThreads * NG), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, NG, NW, T, PRECISE, PAIR>), dim3((unsigned)blocks),
+                     dim3(64 * NW * NG), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, typename T, bool PRECISE>
-hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
+hipError_t launch_one(const PrefillParams& p0, hipStream_t stream) {
+  PrefillParams p = p0;
+  if constexpr (D <= 128) {
+    // Large launches: eight-wave workgroups of 256 query rows share each K/V tile, as long
+    // as that still leaves at least four workgroups per CU.
+    p.bq = 256 / p.group;
+    const int64_t blocks8 = (int64_t)((p.seqlen_q + p.bq - 1) / p.bq) * p.hkv * p.batch;
+    if (blocks8 >= 4 * (int64_t)std::max(p.cus, 1)) {
+      if (blocks8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+      return launch_ng<D, 1, 8, T, PRECISE>(p, blocks8, stream);
+    }
+  }
+  p.bq = 128 / p.group;
   const int64_t nq = (p.seqlen_q + p.bq - 1) / p.bq;
   const int64_t blocks = nq * p.hkv * p.batch;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -448,12 +461,12 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
       // Two-group workgroups fill a CU each. Under a causal mask, pair a heavy and a
       // light query block per workgroup when that still leaves a workgroup per CU.
       if (nq > 1 && blocks >= 2 * (int64_t)std::max(p.cus, 1)) {
-        return launch_ng<D, 2, T, PRECISE, true>(p, (nq + 1) / 2 * p.hkv * p.batch, stream);
+        return launch_ng<D, 2, 4, T, PRECISE, true>(p, (nq + 1) / 2 * p.hkv * p.batch, stream);
       }
-      return launch_ng<D, 2, T, PRECISE>(p, blocks, stream);
+      return launch_ng<D, 2, 4, T, PRECISE>(p, blocks, stream);
     }
   }
-  return launch_ng<D, 1, T, PRECISE>(p, blocks, stream);
+  return launch_ng<D, 1, 4, T, PRECISE>(p, blocks, stream);
 }
 
 template <int D>

@@ -121,11 +121,12 @@ def test_prefill_deterministic():
     np.testing.assert_array_equal(a, b)
 
 
-# Causal launches of fewer than 2048 workgroups split each workgroup's key range over two
-# groups (the small causal cases above); larger launches, and every non-causal one, run a
-# single group per workgroup. On a device with 256 compute units, causal two-group
-# launches of at least 512 query blocks also pair a heavy and a light query block per
-# workgroup; the paired cases below include an odd block count (a middle block alone).
+# Launch forms (d <= 128, a device with 256 compute units): launches with at least 1024
+# eight-wave workgroups of 256 query rows take that form; otherwise causal launches of
+# fewer than 2048 four-wave workgroups split each workgroup's key range over two groups
+# (the small causal cases above), pairing a heavy and a light query block per workgroup
+# from 512 query blocks on, and the rest run one four-wave group per workgroup. The paired
+# cases below include an odd block count (a middle block alone).
 PAIRED = [
     P("f16_d128_causal_paged_paired_odd", 1, 32, 8, 2080, 2080, 128, "f16", True, "paged"),
     P("bf16_d64_causal_paged_paired_chunked", 2, 32, 8, 1030, 1100, 64, "bf16", True, "paged",
@@ -147,22 +148,27 @@ def test_prefill_paired_sampled(case):
     assert err <= tolerance(case)
 
 
-ONE_GROUP = [
-    P("f16_d64_causal_paged_2048wg", 4, 64, 64, 1024, 1024, 64, "f16", True, "paged"),
-    P("bf16_d128_noncausal_dense_2048wg", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense",
+EIGHT_WAVE = [
+    P("f16_d64_causal_paged_1024wg8", 4, 64, 64, 1024, 1024, 64, "f16", True, "paged"),
+    P("bf16_d128_noncausal_dense_1024wg8", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense",
       seqlens_k=(1100, 1000, 999, 64, 1, 700, 1100, 130)),
+    P("bf16_d128_gqa8_causal_paged_ragged_wg8", 2, 32, 4, 4100, 4100, 128, "bf16", True, "paged",
+      seqlens_k=(4100, 3000)),
+    P("f16_d64_noncausal_dense_bhsd_cross_wg8", 4, 16, 16, 4100, 333, 64, "f16", False, "dense",
+      layout="bhsd"),
 ]
 
 
-@pytest.mark.parametrize("case", ONE_GROUP, ids=lambda c: c.name)
-def test_prefill_one_group_sampled(case):
+@pytest.mark.parametrize("case", EIGHT_WAVE, ids=lambda c: c.name)
+def test_prefill_eight_wave_sampled(case):
     say(f"prefill parity (sampled rows) {case}")
     inp = make_prefill_inputs(case, seed=5)
     O, _ = gpu_prefill(inp)
-    rows = np.unique(np.concatenate([[0, 31, 32, 63, 64, 127, 128, case.seqlen_q - 1],
+    rows = np.unique(np.concatenate([[0, 31, 32, 63, 64, 127, 128, 255, 256, 1099, 1100, case.seqlen_q - 1],
                                      np.random.default_rng(1).choice(case.seqlen_q, 24, replace=False)]))
+    rows = rows[rows < case.seqlen_q]
     Oref, _ = oracle_prefill(inp, q_index=rows)
-    err = max_abs_err(O[:, rows], Oref)
+    err = max_abs_err(O[:, :, rows] if case.layout == "bhsd" else O[:, rows], Oref)
     say(f"  max abs err {err:.3e} over {rows.size} rows x all (b, h)")
     assert err <= tolerance(case)
 
