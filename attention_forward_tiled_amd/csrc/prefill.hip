@@ -134,6 +134,13 @@ void prefill_kernel(const PrefillParams p) {
     const int row = (wave * NIW + k) * RPI + r_in;
     dma_off[k] = (uint32_t)((row * rs + ((pc ^ swz<D>(row)) << 3)) * 2);
   }
+  // this lane's Q fragments (B operand of S^T) for the rows set by rpos, rh, rok
+  auto load_q = [&]() {
+    const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (qrow0 + rpos) * p.q_ss;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = rok ? ldg16(qp + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
+  };
+
   const uint32_t smem_base = lds_addr(smem) + grp * 2 * 2 * TILE * 2;
   const char* gsmem = reinterpret_cast<const char*>(smem) + grp * 2 * 2 * TILE * 2;
 
@@ -325,16 +332,15 @@ void prefill_kernel(const PrefillParams p) {
     if (it == 1 && qblk >= nq - 1 - unit) break;   // the middle block of an odd count
     q0 = qblk * p.bq;
 
-    // ---- this lane's query row and its Q fragments (B operand of S^T)
+    // ---- this lane's query row and its Q fragments (B operand of S^T); the second item's
+    // fragments were requested before the first item's merge and store
     {
       const int r = wave * 32 + lq;
       const int hig = r / p.bq;
       rpos = q0 + (r - hig * p.bq);
       rh = kvh * p.group + hig;
       rok = hig < p.group && rpos < sq;
-      const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (qrow0 + rpos) * p.q_ss;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[s] = rok ? ldg16(qp + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      if (it == 0) load_q();
     }
 
     // ---- tile range: [0, n_full) need no masking, [n_full, n_tiles) straddle a boundary;
@@ -360,6 +366,20 @@ void prefill_kernel(const PrefillParams p) {
     for (int i = 0; i < h; i += 2) {
       step(i, std::integral_constant<int, 0>{});
       if (i + 1 < h) step(i + 1, std::integral_constant<int, 1>{});
+    }
+
+    if constexpr (PAIR) {
+      // Q of the second item (the registers are free once the last tile is done): its
+      // load overlaps this item's merge and store.
+      if (it == 0 && unit < nq - 1 - unit) {
+        const int r = wave * 32 + lq;
+        const int hig = r / p.bq;
+        const int pos = unit * p.bq + (r - hig * p.bq);
+        const bool ok = hig < p.group && pos < sq;
+        const uint16_t* qp = p.q + b * p.q_sb + (int64_t)(kvh * p.group + hig) * p.q_sh + (qrow0 + pos) * p.q_ss;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[s] = ok ? ldg16(qp + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      }
     }
 
     if constexpr (NG == 2) {
