@@ -156,6 +156,12 @@ EIGHT_WAVE = [
       seqlens_k=(4100, 3000)),
     P("f16_d64_noncausal_dense_bhsd_cross_wg8", 4, 16, 16, 4100, 333, 64, "f16", False, "dense",
       layout="bhsd"),
+    # group sizes that leave rows of a 256-row workgroup unused (G = 3: 85 positions x 3
+    # heads; G = 6: 42 x 6) and a narrow one (G = 32: 8 positions x 32 heads)
+    P("bf16_d128_gqa3_causal_paged_wg8", 3, 12, 4, 8200, 8200, 128, "bf16", True, "paged",
+      seqlens_k=(8200, 5000, 7777)),
+    P("f16_d64_gqa6_noncausal_dense_wg8", 4, 24, 4, 5000, 700, 64, "f16", False, "dense"),
+    P("bf16_d128_gqa32_causal_paged_wg8", 4, 64, 2, 1100, 1100, 128, "bf16", True, "paged"),
 ]
 
 
