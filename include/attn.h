@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,   /* an argument is out of its documented domain */
-  ATTN_ERR_UNSUPPORTED = 2,   /* a valid combination this build does not implement */
+  ATTN_ERR_UNSUPPORTED = 2,   /* a valid combination the library does not implement */
   ATTN_ERR_LAUNCH = 3,        /* the HIP runtime refused the launch */
   ATTN_ERR_NO_DEVICE = 4      /* no usable HIP device */
 } attn_status_t;
