@@ -169,3 +169,30 @@ def test_combine_bf16_output_rounding(mode):
     Oref, _ = oracle.lse_combine(po.astype(np.float64), pl.astype(np.float64))
     assert max_abs_err(to_f64(o), round_bf16(Oref, mode)) <= 4e-2
     check_bf16_rounding(to_f64(o), to_f64(o32), mode)
+
+
+def test_decode_long_context():
+    # 256k and 128k-1 keys: 4096 pages per sequence and KV head, a ragged last page
+    case = DecodeCase("bf16_long_context", 2, 8, 2, 128, "bf16", lengths_fixed=(262144, 131071))
+    inp = make_decode_inputs(case, seed=10)
+    Oref, lref = oracle_decode(inp)
+    for s in (1, 16):
+        say(f"decode long context num_splits={s}")
+        O, lse = gpu_decode(inp, s, with_lse=True)
+        assert max_abs_err(O, Oref) <= TOL[case.dtype]
+        assert np.abs(lse - lref).max() <= 1e-3
+
+
+def test_decode_large_batch():
+    # more sequences than the plan kernel has threads (several sequences per thread)
+    lens = tuple(int(x) for x in np.random.default_rng(4).integers(0, 400, size=2500))
+    case = DecodeCase("f16_large_batch", 2500, 4, 2, 64, "f16", lengths_fixed=lens)
+    inp = make_decode_inputs(case, seed=11)
+    Oref, lref = oracle_decode(inp)
+    for s in (1, 8):
+        say(f"decode large batch num_splits={s}")
+        O, lse = gpu_decode(inp, s, with_lse=True)
+        assert max_abs_err(O, Oref) <= TOL[case.dtype]
+        fin = np.isfinite(lref)
+        assert (np.isneginf(lse) == ~fin).all()
+        assert np.abs(lse[fin] - lref[fin]).max() <= 1e-3

@@ -243,3 +243,17 @@ def test_prefill_packed_queries(case, q_lens):
         fin = np.isfinite(lr)
         assert (np.isneginf(lg) == np.isneginf(lr)).all()
         assert np.abs(lg[fin] - lr[fin]).max(initial=0.0) <= lse_tolerance(case)
+
+
+def test_prefill_long_keys():
+    # a short chunk of queries against 128k keys (2048 pages in the table), all rows checked
+    case = P("bf16_d128_causal_paged_128k", 1, 8, 2, 100, 131072, 128, "bf16", True, "paged",
+             seqlens_k=(131000,))
+    say(f"prefill parity {case}")
+    inp = make_prefill_inputs(case, seed=12)
+    O, lse = gpu_prefill(inp, with_lse=True)
+    Oref, lref = oracle_prefill(inp)
+    err = max_abs_err(O, Oref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= tolerance(case)
+    assert np.abs(lse - lref).max() <= lse_tolerance(case)
