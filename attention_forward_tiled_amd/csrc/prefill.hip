@@ -145,7 +145,10 @@ void prefill_kernel(const PrefillParams p) {
   const char* gsmem = reinterpret_cast<const char*>(smem) + grp * 2 * 2 * TILE * 2;
 
   // Copy tile j into this group's LDS stage `stage`. Rows past the key length, and every
-  // row of a page whose id is out of range, are fetched from the zero block instead.
+  // row of a page whose id is out of range, are fetched from the zero block instead; the
+  // keys of such a page are left out altogether (bit `stage` of stage_ok is cleared and
+  // the tile is skipped), as in the decode kernels.
+  uint32_t stage_ok = 3u;
   auto issue_tile = [&](int j, int stage) {
     int64_t base;
     bool page_ok = true;
@@ -158,6 +161,7 @@ void prefill_kernel(const PrefillParams p) {
     } else {
       base = b * p.kv_sb + kvh * p.kv_sh + (int64_t)j * kPage * p.kv_ss;
     }
+    stage_ok = page_ok ? (stage_ok | (1u << stage)) : (stage_ok & ~(1u << stage));
     const uint32_t ks = smem_base + stage * 2 * TILE * 2;
     const uint32_t vs = ks + TILE * 2;
     if (page_ok && (j + 1) * kPage <= L) {
@@ -323,8 +327,10 @@ void prefill_kernel(const PrefillParams p) {
     __syncthreads();
     const int j = j0 + i;
     if (j + 1 < j1) issue_tile(j + 1, STAGE ^ 1);
-    if (j < n_full) compute(j, stage_c, Full{});
-    else if (j < j1) compute(j, stage_c, Masked{});
+    if ((stage_ok >> STAGE) & 1u) {
+      if (j < n_full) compute(j, stage_c, Full{});
+      else if (j < j1) compute(j, stage_c, Masked{});
+    }
   };
 
   for (int it = 0; it < (PAIR ? 2 : 1); ++it) {

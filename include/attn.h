@@ -22,9 +22,10 @@
  *    arguments are reported even on a machine without a GPU. A non-OK status
  *    leaves a message readable with attn_last_error() (thread-local).
  *  - Values stored in the device buffers are not validated (that would need a
- *    synchronising copy): out-of-range page ids are treated as empty pages and
- *    key lengths are clamped to their stated host-side bounds, so a bad table
- *    gives wrong numbers, never an out-of-bounds access.
+ *    synchronising copy): the 64 keys of a page whose id is outside
+ *    [0, num_blocks) are left out of the softmax, and key lengths are clamped to
+ *    their stated host-side bounds, so a bad table gives wrong numbers, never an
+ *    out-of-bounds access.
  *  - Outputs in fp16 / bf16 are rounded to nearest, ties to even, unless the call's
  *    o_round field selects another mode for a bf16 output (attn_round_t).
  */

@@ -196,3 +196,24 @@ def test_decode_large_batch():
         fin = np.isfinite(lref)
         assert (np.isneginf(lse) == ~fin).all()
         assert np.abs(lse[fin] - lref[fin]).max() <= 1e-3
+
+
+@pytest.mark.parametrize("splits", [1, 16])
+def test_decode_invalid_page_ids_are_left_out(splits):
+    import dataclasses
+    case = DecodeCase("bf16_bad_ids", 2, 8, 2, 128, "bf16", lengths_fixed=(1000, 333))
+    inp = make_decode_inputs(case, seed=15)
+    nb = inp.k_cache.shape[0]
+    bad = inp.block_table.copy()
+    bad[0, 7] = nb + 1
+    bad[1, 2] = -5
+    say(f"decode with invalid page ids, num_splits={splits}")
+    O, _ = gpu_decode(dataclasses.replace(inp, block_table=bad), splits)
+    table = np.zeros_like(inp.block_table)
+    keep0 = [j for j in range(16) if j != 7]
+    keep1 = [j for j in range(6) if j != 2]
+    table[0, :len(keep0)] = inp.block_table[0, keep0]
+    table[1, :len(keep1)] = inp.block_table[1, keep1]
+    ref = dataclasses.replace(inp, block_table=table, seqlens_k=np.array([1000 - 64, 333 - 64], dtype=np.int32))
+    Oref, _ = oracle_decode(ref)
+    assert max_abs_err(O, Oref) <= TOL[case.dtype]

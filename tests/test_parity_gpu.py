@@ -257,3 +257,26 @@ def test_prefill_long_keys():
     say(f"  max abs err {err:.3e}")
     assert err <= tolerance(case)
     assert np.abs(lse - lref).max() <= lse_tolerance(case)
+
+
+def test_prefill_invalid_page_ids_are_left_out():
+    # a page id outside [0, num_blocks) drops that page's 64 keys (no out-of-bounds read);
+    # non-causal, so the expected result is the oracle on the table without those pages
+    import dataclasses
+    case = P("bf16_d128_noncausal_paged_bad_ids", 2, 8, 2, 100, 640, 128, "bf16", False, "paged",
+             seqlens_k=(640, 400))
+    inp = make_prefill_inputs(case, seed=14)
+    nb = inp.k.shape[0]
+    bad = inp.block_table.copy()
+    bad[0, 3] = -1
+    bad[1, 5] = nb + 7
+    say(f"prefill parity with invalid page ids {case}")
+    O, _ = gpu_prefill(dataclasses.replace(inp, block_table=bad))
+    keep0 = [j for j in range(10) if j != 3]
+    keep1 = [j for j in range(7) if j != 5]
+    table = np.zeros_like(inp.block_table)
+    table[0, :len(keep0)] = inp.block_table[0, keep0]
+    table[1, :len(keep1)] = inp.block_table[1, keep1]
+    lens = np.array([640 - 64, 400 - 64], dtype=np.int32)
+    Oref, _ = oracle_prefill(dataclasses.replace(inp, block_table=table, seqlens_k=lens))
+    assert max_abs_err(O, Oref) <= tolerance(case)
