@@ -128,12 +128,18 @@ void prefill_kernel(const PrefillParams p) {
   const bool paged = p.block_table != nullptr;
   const int64_t rs = paged ? (int64_t)p.hkv * D : p.kv_ss;   // elements between key rows
   const int r_in = lane / CPR, pc = lane % CPR;
-  uint32_t dma_off[NIW];
+  // Eight-wave form: waves 0-3 (one per SIMD) copy the rows of wave pairs (2w, 2w+1), so
+  // that on every SIMD one wave starts its products while the other issues copies.
+  constexpr int CW = NW == 8 ? 2 : 1;          // copy shares per issuing wave
+  const int cw0 = NW == 8 ? 2 * (wave & 3) : wave;
+  uint32_t dma_off[CW][NIW];
 #pragma unroll
-  for (int k = 0; k < NIW; ++k) {
-    const int row = (wave * NIW + k) * RPI + r_in;
-    dma_off[k] = (uint32_t)((row * rs + ((pc ^ swz<D>(row)) << 3)) * 2);
-  }
+  for (int v = 0; v < CW; ++v)
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+      const int row = ((cw0 + v) * NIW + k) * RPI + r_in;
+      dma_off[v][k] = (uint32_t)((row * rs + ((pc ^ swz<D>(row)) << 3)) * 2);
+    }
   // this lane's Q fragments (B operand of S^T) for the rows set by rpos, rh, rok
   auto load_q = [&]() {
     const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (qrow0 + rpos) * p.q_ss;
@@ -164,21 +170,26 @@ void prefill_kernel(const PrefillParams p) {
     stage_ok = page_ok ? (stage_ok | (1u << stage)) : (stage_ok & ~(1u << stage));
     const uint32_t ks = smem_base + stage * 2 * TILE * 2;
     const uint32_t vs = ks + TILE * 2;
+    if (NW == 8 && wave >= 4) return;
     if (page_ok && (j + 1) * kPage <= L) {
 #pragma unroll
-      for (int k = 0; k < NIW; ++k) {
-        const int i = wave * NIW + k;
-        dma16_s(p.k + base, dma_off[k], ks + i * 1024);
-        dma16_s(p.v + base, dma_off[k], vs + i * 1024);
-      }
+      for (int v = 0; v < CW; ++v)
+#pragma unroll
+        for (int k = 0; k < NIW; ++k) {
+          const int i = (cw0 + v) * NIW + k;
+          dma16_s(p.k + base, dma_off[v][k], ks + i * 1024);
+          dma16_s(p.v + base, dma_off[v][k], vs + i * 1024);
+        }
     } else {
 #pragma unroll
-      for (int k = 0; k < NIW; ++k) {
-        const int i = wave * NIW + k;
-        const bool ok = page_ok && (j * kPage + (i * RPI + r_in) < L);
-        dma16_v(ok ? p.k + base + dma_off[k] / 2 : kZeroChunk, ks + i * 1024);
-        dma16_v(ok ? p.v + base + dma_off[k] / 2 : kZeroChunk, vs + i * 1024);
-      }
+      for (int v = 0; v < CW; ++v)
+#pragma unroll
+        for (int k = 0; k < NIW; ++k) {
+          const int i = (cw0 + v) * NIW + k;
+          const bool ok = page_ok && (j * kPage + (i * RPI + r_in) < L);
+          dma16_v(ok ? p.k + base + dma_off[v][k] / 2 : kZeroChunk, ks + i * 1024);
+          dma16_v(ok ? p.v + base + dma_off[v][k] / 2 : kZeroChunk, vs + i * 1024);
+        }
     }
   };
 
