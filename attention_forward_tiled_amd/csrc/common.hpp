@@ -178,7 +178,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // that publishes the stage.
 __device__ __forceinline__ void dma16_v(const uint16_t* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 
 // Same copy with a wave-uniform base in SGPRs and a per-lane 32-bit byte offset.
@@ -191,7 +191,7 @@ __device__ __forceinline__ void dma16_s(const uint16_t* base, uint32_t voff, uin
   const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"((const uint16_t*)bs), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
+               : "memory", "m0");
 }
 
 // Read-only device int through the constant address space, so it becomes a scalar load.
