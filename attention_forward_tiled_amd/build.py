@@ -37,9 +37,16 @@ def flags() -> list:
             f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
 
 
+# Per-source additions. The prefill tile loop takes per-lane maxima of its scores on every
+# tile; no NaN can reach them (masked scores are -inf and key rows past a sequence's
+# length are read from a zero block), so the compiler is told it need not quiet
+# signalling NaNs before each max (one instruction per two scores saved).
+EXTRA_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
