@@ -175,10 +175,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // global_load_lds_dwordx4 with a per-lane 64-bit address: lane l's 16 bytes land at LDS
 // byte lds + 16 * l. Issued from inline asm so that the compiler does not fence LDS reads
 // of the other stage on it; completion is awaited explicitly (vmcnt) before the barrier
-// that publishes the stage.
+// that publishes the stage. The asm sets m0, which the compiler reserves (it cannot be
+// named as clobbered) and which the generated code of these kernels uses nowhere else.
 __device__ __forceinline__ void dma16_v(const uint16_t* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
 // Same copy with a wave-uniform base in SGPRs and a per-lane 32-bit byte offset.
@@ -191,7 +192,7 @@ __device__ __forceinline__ void dma16_s(const uint16_t* base, uint32_t voff, uin
   const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"((const uint16_t*)bs), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
+               : "memory");
 }
 
 // Read-only device int through the constant address space, so it becomes a scalar load.
