@@ -148,7 +148,9 @@ void prefill_kernel(const PrefillParams p) {
   };
 
   const uint32_t smem_base = lds_addr(smem) + grp * 2 * 2 * TILE * 2;
-  const char* gsmem = reinterpret_cast<const char*>(smem) + grp * 2 * 2 * TILE * 2;
+  // The group's byte offset is folded into the per-lane read offsets below, so that
+  // the stage bases stay compile-time constants (immediate offsets of the LDS reads).
+  const uint32_t goff = grp * 2 * 2 * TILE * 2;
 
   // Copy tile j into this group's LDS stage `stage`. Rows past the key length, and every
   // row of a page whose id is out of range, are fetched from the zero block instead; the
@@ -197,7 +199,7 @@ void prefill_kernel(const PrefillParams p) {
   // K A-operand for S^T: row 32*kb + lq (kb enters as an immediate), chunk 2*s + half.
   uint32_t koff[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) koff[s] = lq * ROWB + (((2 * s + half) ^ swz<D>(lq)) << 4);
+  for (int s = 0; s < KS; ++s) koff[s] = goff + lq * ROWB + (((2 * s + half) ^ swz<D>(lq)) << 4);
   // V^T A-operand via transpose reads: lane (g = lane/16, j = lane%16) addresses row
   // 16*t + 8*h + 4*(g/2) + j/4 (t enters as an immediate) at column 32*db + 16*(g%2) + 4*(j%4).
   const int tg = lane >> 4, tj = lane & 15;
@@ -208,7 +210,7 @@ void prefill_kernel(const PrefillParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int col = 32 * db + 16 * (tg & 1) + 4 * (tj & 3);
-      voff[hh][db] = row * ROWB + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+      voff[hh][db] = goff + row * ROWB + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
     }
   }
 
@@ -220,7 +222,7 @@ void prefill_kernel(const PrefillParams p) {
   auto compute = [&](int j, auto stage_c, auto mask_c) {
     constexpr int STAGE = decltype(stage_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    const char* ks = gsmem + STAGE * 2 * TILE * 2;
+    const char* ks = reinterpret_cast<const char*>(smem) + STAGE * 2 * TILE * 2;
     const char* vs = ks + TILE * 2;
 
     // scores of keys 32*kb + 8*g + 4*half + i, at sc[kb][4*g + i]
