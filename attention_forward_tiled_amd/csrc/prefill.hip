@@ -7,9 +7,14 @@
 // section 5. Scores are handled in the base-2 domain (s * tau * log2 e, exp2).
 //
 // How it is mapped onto CDNA4:
-//   * A workgroup is 4 waves and owns 128 query rows that share one KV head: for a
-//     GQA group of G query heads it takes bq = 128 / G positions of every head of the
-//     group, so each K/V tile brought into LDS serves all G heads.
+//   * A group of NW waves owns 32 * NW query rows that share one KV head: for a GQA
+//     group of G query heads it takes 32 * NW / G positions of every head of the group,
+//     so each K/V tile brought into LDS serves all G heads. Three launch forms (chosen
+//     on the host, see launch_one): eight waves / 256 rows for large launches (twice the
+//     rows per copied tile); two groups of four waves splitting one block's key tiles
+//     (merged through LDS) for causal launches with few blocks, optionally pairing a
+//     heavy and a light block per workgroup; otherwise four waves / 128 rows, two
+//     workgroups per CU.
 //   * Each wave owns 32 rows. Scores are produced transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16: K comes from LDS as the A operand and Q stays in registers
 //     as the B operand for the whole kernel. The accumulator then holds, per lane, one
@@ -23,7 +28,9 @@
 //     in memory (row-major, 16-byte chunks XOR-swizzled by row to spread banks), and
 //     are copied there by global_load_lds_dwordx4 without passing through registers.
 //   * Two LDS stages: tile j+1 is in flight while tile j is consumed; one barrier per
-//     tile. The main loop is unrolled by two so every LDS offset is an immediate.
+//     tile. The main loop is unrolled by two so every LDS offset is an immediate. In
+//     the eight-wave form one wave per SIMD issues the copies (the address unit takes
+//     them one at a time; the SIMD's other wave meanwhile starts its products).
 //   * Tiles entirely inside the visible region run a loop with no masking code; the
 //     tiles that straddle the causal diagonal or the key length run a second loop that
 //     masks scores and fetches rows past the key length from a block of zeros (NaN in
