@@ -157,3 +157,16 @@ def test_valid_call_without_device_reports_no_device(lib):
     assert lib.attn_prefill_fwd(ctypes.byref(prefill_args()), None) == _lib.ATTN_ERR_NO_DEVICE
     assert lib.attn_decode_fwd(ctypes.byref(decode_args()), None) == _lib.ATTN_ERR_NO_DEVICE
     assert lib.attn_splitkv_combine(ctypes.byref(combine_args()), None) == _lib.ATTN_ERR_NO_DEVICE
+
+
+def test_missing_library_raises(tmp_path, monkeypatch):
+    """No fallback: with libattn.so absent, the binding refuses to run at all."""
+    from attention_forward_tiled_amd import _lib
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattn.so"))
+    monkeypatch.setattr(_lib.load, "__defaults__", (str(tmp_path / "libattn.so"),))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()
+    from attention_forward_tiled_amd import attn_decode_workspace_bytes
+    with pytest.raises(RuntimeError, match="not built"):
+        attn_decode_workspace_bytes(1, 4, 2, 64)
