@@ -162,6 +162,11 @@ EIGHT_WAVE = [
       seqlens_k=(8200, 5000, 7777)),
     P("f16_d64_gqa6_noncausal_dense_wg8", 4, 24, 4, 5000, 700, 64, "f16", False, "dense"),
     P("bf16_d128_gqa32_causal_paged_wg8", 4, 64, 2, 1100, 1100, 128, "bf16", True, "paged"),
+    # precise P (hi + lo products) with an fp32 output, in the eight-wave form
+    P("f16_d64_precise_f32out_dense_wg8", 4, 16, 16, 4096, 4096, 64, "f16", True, "dense",
+      out_dtype="f32", precise=True),
+    P("bf16_d128_precise_f32out_paged_wg8", 2, 32, 8, 4096, 3000, 128, "bf16", False, "paged",
+      out_dtype="f32", precise=True, seqlens_k=(3000, 1999)),
 ]
 
 
@@ -205,6 +210,9 @@ VARLEN = [
        seqlens_k=(130, 7, 130)), (33, 200, 1)),
     (P("bf16_d128_causal_paged_gqa4_varlen", 3, 16, 4, 700, 900, 128, "bf16", True, "paged",
        seqlens_k=(900, 700, 333)), (700, 129, 333)),
+    # eight-wave form (max_seqlen_q 4096: 16 x 8 heads x 8 sequences = 1024 workgroups)
+    (P("f16_d64_noncausal_dense_varlen_wg8", 8, 8, 8, 4096, 1000, 64, "f16", False, "dense",
+       seqlens_k=(200, 64, 1, 130, 700, 5, 64, 999)), (4096, 0, 1, 255, 256, 257, 1000, 3000)),
 ]
 
 
@@ -259,12 +267,20 @@ def test_prefill_long_keys():
     assert np.abs(lse - lref).max() <= lse_tolerance(case)
 
 
-def test_prefill_invalid_page_ids_are_left_out():
+BAD_ID_CASES = [
+    P("bf16_d128_noncausal_paged_bad_ids", 2, 8, 2, 100, 640, 128, "bf16", False, "paged",
+      seqlens_k=(640, 400)),
+    # eight-wave form: 32 x 8 heads x 4 sequences = 1024 workgroups
+    P("f16_d64_noncausal_paged_bad_ids_wg8", 4, 8, 8, 8192, 640, 64, "f16", False, "paged",
+      seqlens_k=(640, 400, 640, 64)),
+]
+
+
+@pytest.mark.parametrize("case", BAD_ID_CASES, ids=lambda c: c.name)
+def test_prefill_invalid_page_ids_are_left_out(case):
     # a page id outside [0, num_blocks) drops that page's 64 keys (no out-of-bounds read);
     # non-causal, so the expected result is the oracle on the table without those pages
     import dataclasses
-    case = P("bf16_d128_noncausal_paged_bad_ids", 2, 8, 2, 100, 640, 128, "bf16", False, "paged",
-             seqlens_k=(640, 400))
     inp = make_prefill_inputs(case, seed=14)
     nb = inp.k.shape[0]
     bad = inp.block_table.copy()
@@ -274,9 +290,11 @@ def test_prefill_invalid_page_ids_are_left_out():
     O, _ = gpu_prefill(dataclasses.replace(inp, block_table=bad))
     keep0 = [j for j in range(10) if j != 3]
     keep1 = [j for j in range(7) if j != 5]
-    table = np.zeros_like(inp.block_table)
+    table = inp.block_table.copy()
+    table[:2] = 0
     table[0, :len(keep0)] = inp.block_table[0, keep0]
     table[1, :len(keep1)] = inp.block_table[1, keep1]
-    lens = np.array([640 - 64, 400 - 64], dtype=np.int32)
+    lens = inp.seqlens_k.copy()
+    lens[:2] -= 64
     Oref, _ = oracle_prefill(dataclasses.replace(inp, block_table=table, seqlens_k=lens))
     assert max_abs_err(O, Oref) <= tolerance(case)
