@@ -150,19 +150,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
     const uint32_t vs = ks + TILE_B;
     if (page_ok && key0 + kPage <= end) {
 #pragma unroll
-      for (int i = 0; i < NIW; ++i) dma16_s(p.k + base, dma_off[i], ks + (wave * NIW + i) * 1024);
+      for (int i = 0; i < NIW; ++i) dma16_s<true>(p.k + base, dma_off[i], ks + (wave * NIW + i) * 1024);
 #pragma unroll
-      for (int i = 0; i < NIW; ++i) dma16_s(p.v + base, dma_off[i], vs + (wave * NIW + i) * 1024);
+      for (int i = 0; i < NIW; ++i) dma16_s<true>(p.v + base, dma_off[i], vs + (wave * NIW + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < end;
-        dma16_v(ok ? p.k + base + dma_off[i] / 2 : kZeroChunk, ks + (wave * NIW + i) * 1024);
+        dma16_v<true>(ok ? p.k + base + dma_off[i] / 2 : kZeroChunk, ks + (wave * NIW + i) * 1024);
       }
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < end;
-        dma16_v(ok ? p.v + base + dma_off[i] / 2 : kZeroChunk, vs + (wave * NIW + i) * 1024);
+        dma16_v<true>(ok ? p.v + base + dma_off[i] / 2 : kZeroChunk, vs + (wave * NIW + i) * 1024);
       }
     }
   };
@@ -414,19 +414,19 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
     const uint32_t qs = vs + TILE_B;
     if (page_ok && key0 + kPage <= c.L) {
 #pragma unroll
-      for (int i = 0; i < NIW; ++i) dma16_s(p.k + base, dma_off[i], ks + (wave * NIW + i) * 1024);
+      for (int i = 0; i < NIW; ++i) dma16_s<true>(p.k + base, dma_off[i], ks + (wave * NIW + i) * 1024);
 #pragma unroll
-      for (int i = 0; i < NIW; ++i) dma16_s(p.v + base, dma_off[i], vs + (wave * NIW + i) * 1024);
+      for (int i = 0; i < NIW; ++i) dma16_s<true>(p.v + base, dma_off[i], vs + (wave * NIW + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < c.L;
-        dma16_v(ok ? p.k + base + dma_off[i] / 2 : kZeroChunk, ks + (wave * NIW + i) * 1024);
+        dma16_v<true>(ok ? p.k + base + dma_off[i] / 2 : kZeroChunk, ks + (wave * NIW + i) * 1024);
       }
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const bool ok = page_ok && key0 + (wave * NIW + i) * RPI + r_in < c.L;
-        dma16_v(ok ? p.v + base + dma_off[i] / 2 : kZeroChunk, vs + (wave * NIW + i) * 1024);
+        dma16_v<true>(ok ? p.v + base + dma_off[i] / 2 : kZeroChunk, vs + (wave * NIW + i) * 1024);
       }
     }
     const uint16_t* qb = p.q + ((int64_t)c.b * p.hq + (int64_t)kvh * G) * D;
