@@ -76,7 +76,10 @@ typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
  * the causal mask is aligned to the bottom-right corner (same page, section 4),
  * and key tiles entirely in a query tile's future are skipped. Query head h reads
  * KV head floor(h / G), G = num_heads_q / num_heads_kv (GQA; same page, section 5).
- * A row with no visible key gets O = 0 and lse = -inf.
+ * A row with no visible key gets O = 0 and lse = -inf. Q and the visible K/V rows must
+ * be finite (NaN or infinity there gives unspecified values, not necessarily NaN); key
+ * rows that are not visible, such as the unused tail of a sequence's last page, may
+ * hold anything and are never read into the arithmetic.
  *
  * Fields:
  *  q        [B, S_q, Hq, d] (BSHD) or [B, Hq, S_q, d] (BHSD), qkv_dtype.
