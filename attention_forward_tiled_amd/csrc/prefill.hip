@@ -491,9 +491,13 @@ hipError_t launch_one(const PrefillParams& p0, hipStream_t stream) {
   if constexpr (D <= 128) {
     // Large launches: eight-wave workgroups of 256 query rows share each K/V tile, as long
     // as that still leaves at least four workgroups per CU.
+    // Causal MHA below 8192 keys keeps the four-wave blocks: an eight-wave block of G = 1
+    // spans 256 positions, four of its tiles straddle the diagonal, and at these lengths
+    // that costs more than the shared copies save (8% at 4096, even at 8192).
+    const bool diag_heavy = p.causal && p.group == 1 && p.seqlen_k < 8192;
     p.bq = 256 / p.group;
     const int64_t blocks8 = (int64_t)((p.seqlen_q + p.bq - 1) / p.bq) * p.hkv * p.batch;
-    if (blocks8 >= 4 * (int64_t)std::max(p.cus, 1)) {
+    if (!diag_heavy && blocks8 >= 4 * (int64_t)std::max(p.cus, 1)) {
       if (blocks8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
       return launch_ng<D, 1, 8, T, PRECISE>(p, blocks8, stream);
     }

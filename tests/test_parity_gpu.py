@@ -149,7 +149,7 @@ def test_prefill_paired_sampled(case):
 
 
 EIGHT_WAVE = [
-    P("f16_d64_causal_paged_1024wg8", 4, 64, 64, 1024, 1024, 64, "f16", True, "paged"),
+    P("f16_d64_gqa2_causal_paged_1024wg8", 4, 64, 32, 1024, 1024, 64, "f16", True, "paged"),
     P("bf16_d128_noncausal_dense_1024wg8", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense",
       seqlens_k=(1100, 1000, 999, 64, 1, 700, 1100, 130)),
     P("bf16_d128_gqa8_causal_paged_ragged_wg8", 2, 32, 4, 4100, 4100, 128, "bf16", True, "paged",
@@ -163,8 +163,10 @@ EIGHT_WAVE = [
     P("f16_d64_gqa6_noncausal_dense_wg8", 4, 24, 4, 5000, 700, 64, "f16", False, "dense"),
     P("bf16_d128_gqa32_causal_paged_wg8", 4, 64, 2, 1100, 1100, 128, "bf16", True, "paged"),
     # precise P (hi + lo products) with an fp32 output, in the eight-wave form
-    P("f16_d64_precise_f32out_dense_wg8", 4, 16, 16, 4096, 4096, 64, "f16", True, "dense",
+    P("f16_d64_precise_f32out_dense_wg8", 4, 16, 16, 4096, 4096, 64, "f16", False, "dense",
       out_dtype="f32", precise=True),
+    # (not eight-wave) causal MHA below 8192 keys: four-wave blocks, sampled rows
+    P("bf16_d128_causal_mha_dense_4k_wg4", 2, 32, 32, 4096, 4096, 128, "bf16", True, "dense"),
     P("bf16_d128_precise_f32out_paged_wg8", 2, 32, 8, 4096, 3000, 128, "bf16", False, "paged",
       out_dtype="f32", precise=True, seqlens_k=(3000, 1999)),
 ]
