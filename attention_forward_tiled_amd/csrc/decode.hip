@@ -23,7 +23,9 @@
 //     i is consumed. The K/V copies are non-temporal: every page is read once, and
 //     marking the stream so keeps it from displacing reusable cache lines (12% faster).
 //     The persistent variant (decode_stream_kernel, below) is the one used for
-//     num_splits >= 2.
+//     num_splits >= 2. At d = 64 it consumes two pages of a partition per barrier (one
+//     128-key tile), since a page there carries half the bytes for the same chain of
+//     dependent steps.
 //   * All four waves work on the same page, 16 keys each: S^T = K Q^T with
 //     v_mfma_f32_16x16x32 (K rows from LDS as the A operand, the group's query heads
 //     padded to 16 columns as the B operand). The accumulator layout is the B-operand
@@ -323,8 +325,9 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
 }
 
 // Ring depth of the stream kernel: 144 KiB of stages (K tile, V tile, Q block) per
-// workgroup, so one workgroup per CU.
-template <int D> constexpr int kStreamStages = D == 64 ? 7 : (D == 128 ? 4 : 2);
+// workgroup at d = 128 and 256, all 160 KiB at d = 64 (which consumes two pages per
+// barrier); one workgroup per CU.
+template <int D> constexpr int kStreamStages = D == 64 ? 8 : (D == 128 ? 4 : 2);
 
 // Balanced (persistent) split kernel. Workgroup w serves KV head w % Hkv and unit range
 // j = w / Hkv of the plan; the workgroups of the Hkv heads with the same j walk the
@@ -347,6 +350,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
   constexpr int ROWB = D * 2;                // bytes per LDS row
   constexpr int TILE_B = kPage * ROWB;       // bytes per K (or V) tile
   constexpr int STAGE_B = 2 * TILE_B + QIW * kWaves * 1024;
+  constexpr bool kPairs = D == 64;           // two pages consumed per barrier
   static_assert(NST >= 2 && (NST - 2) * PER < 64, "ring depth");
   static_assert(3 * DB * 1024 + 2 * 3 * 64 * 4 <= STAGE_B, "merge buffer");
   static_assert(QIW * kWaves * 1024 >= 16 * ROWB, "Q block");
@@ -474,109 +478,186 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
     if (k + 1 < n_units) advance(ic);
   }
 
+  // End of a partition whose last unit sits in `stage` (consumed by every wave): merge the
+  // four waves' states through that stage, write the partial of run c to its slot and
+  // restart the state empty.
+  auto finish = [&](int stage, const Cursor& c, bool run_end) __attribute__((always_inline)) {
+    const float l_w = rows4_sum(lsum);
+    __syncthreads();
+    float* mb = reinterpret_cast<float*>(ring + stage * STAGE_B);
+    float* m_lds = mb + 3 * DB * 256;
+    float* l_lds = m_lds + 3 * 64;
+    if (wave > 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4v*>(mb + (((wave - 1) * DB + db) * 64 + lane) * 4) = acc[db];
+      m_lds[(wave - 1) * 64 + lane] = m;
+      l_lds[(wave - 1) * 64 + lane] = l_w;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      float mw[4], lw[4];
+      mw[0] = m;
+      lw[0] = l_w;
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        mw[w] = m_lds[(w - 1) * 64 + lane];
+        lw[w] = l_lds[(w - 1) * 64 + lane];
+      }
+      const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+      float sc[4], den = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        sc[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
+        den += sc[w] * lw[w];
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      const int slot = piece_u0 / chunk - c.U / chunk;
+      const int64_t row0 = ((int64_t)c.b * p.hq + (int64_t)kvh * G) * S;
+      if (lr < G) {
+        const int64_t row = row0 + (int64_t)lr * S + slot;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          float4v o = acc[db] * sc[0];
+#pragma unroll
+          for (int w = 1; w < 4; ++w)
+            o += *reinterpret_cast<const float4v*>(mb + (((w - 1) * DB + db) * 64 + lane) * 4) * sc[w];
+          *reinterpret_cast<float4v*>(p.part_o + row * D + 16 * db + 4 * lg) = o * inv;
+        }
+        if (lg == 0) p.part_lse[row] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+      }
+      if (run_end)   // unused partitions of the run
+        for (int e = lane; e < G * S; e += 64) {
+          const int g = e / S, sl = e % S;
+          if (sl > slot) p.part_lse[row0 + (int64_t)g * S + sl] = -INFINITY;
+        }
+    }
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
+  };
+
   int cstage = 0;
-  for (int i = 0; i < n_units; ++i) {
-    wait_pages<PER, NST - 2>(min(NST - 2, n_units - 1 - i));
-    __syncthreads();   // unit i visible to every wave; the stage of unit i - 1 is free
-    if (i + NST - 1 < n_units) {
-      issue(i + NST - 1, ic, istage);
-      istage = istage + 1 == NST ? 0 : istage + 1;
-      if (i + NST < n_units) advance(ic);
-    }
-
-    const char* st = ring + cstage * STAGE_B;
-    float4v s = {0.f, 0.f, 0.f, 0.f};   // S^T: keys 16*wave + 4*lg + j of the page, head lr
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-      s = Op<T>::mfma(as_op<T>(*reinterpret_cast<const u32x4*>(st + koff[k])),
-                      as_op<T>(*reinterpret_cast<const u32x4*>(st + qoff[k])), s);
-
-    const bool page_ok = (page_ok_bits >> (i & 31)) & 1u;
-    const int key = cc.page * kPage + 16 * wave + 4 * lg;
-    float x[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j] = page_ok && key + j < cc.L ? s[j] * p.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[j]);
-    }
-    mx = rows4_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
-    float pr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    const u32x2 pb = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const u32x2 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(st + voff[db]));
-      acc[db] = Op<T>::mfma16k(a, pb, acc[db] * alpha);
-    }
-
-    const bool run_end = cc.page == cc.R - 1;
-    if (run_end || i == n_units - 1) {
-      // ---- end of a partition: merge the waves through this (consumed) stage
-      const float l_w = rows4_sum(lsum);
-      __syncthreads();
-      float* mb = reinterpret_cast<float*>(ring + cstage * STAGE_B);
-      float* m_lds = mb + 3 * DB * 256;
-      float* l_lds = m_lds + 3 * 64;
-      if (wave > 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<float4v*>(mb + (((wave - 1) * DB + db) * 64 + lane) * 4) = acc[db];
-        m_lds[(wave - 1) * 64 + lane] = m;
-        l_lds[(wave - 1) * 64 + lane] = l_w;
+  if constexpr (!kPairs) {
+    for (int i = 0; i < n_units; ++i) {
+      wait_pages<PER, NST - 2>(min(NST - 2, n_units - 1 - i));
+      __syncthreads();   // unit i visible to every wave; the stage of unit i - 1 is free
+      if (i + NST - 1 < n_units) {
+        issue(i + NST - 1, ic, istage);
+        istage = istage + 1 == NST ? 0 : istage + 1;
+        if (i + NST < n_units) advance(ic);
       }
-      __syncthreads();
-      if (wave == 0) {
-        float mw[4], lw[4];
-        mw[0] = m;
-        lw[0] = l_w;
+
+      const char* st = ring + cstage * STAGE_B;
+      float4v s = {0.f, 0.f, 0.f, 0.f};   // S^T: keys 16*wave + 4*lg + j of the page, head lr
 #pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          mw[w] = m_lds[(w - 1) * 64 + lane];
-          lw[w] = l_lds[(w - 1) * 64 + lane];
-        }
-        const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-        float sc[4], den = 0.f;
+      for (int k = 0; k < KS; ++k)
+        s = Op<T>::mfma(as_op<T>(*reinterpret_cast<const u32x4*>(st + koff[k])),
+                        as_op<T>(*reinterpret_cast<const u32x4*>(st + qoff[k])), s);
+
+      const bool page_ok = (page_ok_bits >> (i & 31)) & 1u;
+      const int key = cc.page * kPage + 16 * wave + 4 * lg;
+      float x[4];
+      float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          sc[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
-          den += sc[w] * lw[w];
-        }
-        const float inv = den > 0.f ? 1.f / den : 0.f;
-        const int slot = piece_u0 / chunk - cc.U / chunk;
-        const int64_t row0 = ((int64_t)cc.b * p.hq + (int64_t)kvh * G) * S;
-        if (lr < G) {
-          const int64_t row = row0 + (int64_t)lr * S + slot;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            float4v o = acc[db] * sc[0];
-#pragma unroll
-            for (int w = 1; w < 4; ++w)
-              o += *reinterpret_cast<const float4v*>(mb + (((w - 1) * DB + db) * 64 + lane) * 4) * sc[w];
-            *reinterpret_cast<float4v*>(p.part_o + row * D + 16 * db + 4 * lg) = o * inv;
-          }
-          if (lg == 0) p.part_lse[row] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
-        }
-        if (run_end)   // unused partitions of the run
-          for (int e = lane; e < G * S; e += 64) {
-            const int g = e / S, sl = e % S;
-            if (sl > slot) p.part_lse[row0 + (int64_t)g * S + sl] = -INFINITY;
-          }
+      for (int j = 0; j < 4; ++j) {
+        x[j] = page_ok && key + j < cc.L ? s[j] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[j]);
       }
-      m = -INFINITY;
-      lsum = 0.f;
+      mx = rows4_max(mx);
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      m = m_new;
+      float pr[4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
-      piece_u0 = u_begin + i + 1;
+      for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
+      lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      const u32x2 pb = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(st + voff[db]));
+        acc[db] = Op<T>::mfma16k(a, pb, acc[db] * alpha);
+      }
+
+      const bool run_end = cc.page == cc.R - 1;
+      if (run_end || i == n_units - 1) {
+        finish(cstage, cc, run_end);
+        piece_u0 = u_begin + i + 1;
+      }
+      cstage = cstage + 1 == NST ? 0 : cstage + 1;
+      if (i + 1 < n_units) advance(cc);
     }
-    cstage = cstage + 1 == NST ? 0 : cstage + 1;
-    if (i + 1 < n_units) advance(cc);
+  } else {
+    // d = 64: a page holds half the bytes of a d = 128 page but its consumption is the same
+    // chain of dependent steps (LDS reads, products, cross-lane max, exponentials, products),
+    // which one wave per SIMD cannot hide. Two pages of one partition are therefore taken
+    // per barrier, as one 128-key tile with the two chains interleaved; a unit that ends a
+    // run alone is paired with itself, its second half masked out.
+    int issued = pro;   // units whose copies have been started
+    for (int i = 0; i < n_units;) {
+      const bool two = i + 1 < n_units && cc.page + 1 < cc.R;
+      const int c = two ? 2 : 1;
+      wait_pages<PER, NST - 2>(issued - i - c);
+      __syncthreads();   // units i .. i + c - 1 visible; the stages of earlier units are free
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (issued < n_units && issued - i < NST) {
+          issue(issued, ic, istage);
+          istage = istage + 1 == NST ? 0 : istage + 1;
+          if (++issued < n_units) advance(ic);
+        }
+
+      const char* sa = ring + cstage * STAGE_B;
+      const char* sb = two ? ring + (cstage + 1 == NST ? 0 : cstage + 1) * STAGE_B : sa;
+      float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const auto q = as_op<T>(*reinterpret_cast<const u32x4*>(sa + qoff[k]));
+        s0 = Op<T>::mfma(as_op<T>(*reinterpret_cast<const u32x4*>(sa + koff[k])), q, s0);
+        s1 = Op<T>::mfma(as_op<T>(*reinterpret_cast<const u32x4*>(sb + koff[k])), q, s1);
+      }
+
+      const bool ok0 = (page_ok_bits >> (i & 31)) & 1u;
+      const bool ok1 = two && ((page_ok_bits >> ((i + 1) & 31)) & 1u);
+      const int key = cc.page * kPage + 16 * wave + 4 * lg;
+      float x[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = ok0 && key + j < cc.L ? s0[j] * p.scale_log2 : -INFINITY;
+        x[4 + j] = ok1 && key + kPage + j < cc.L ? s1[j] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, fmaxf(x[j], x[4 + j]));
+      }
+      mx = rows4_max(mx);
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      m = m_new;
+      float pr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(x[j] - m_use);
+      lsum = lsum * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+      const u32x2 pb0 = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
+      const u32x2 pb1 = u32x2{pack2<T>(pr[4], pr[5]), pack2<T>(pr[6], pr[7])};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 a0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(sa + voff[db]));
+        const u32x2 a1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(sb + voff[db]));
+        acc[db] = Op<T>::mfma16k(a1, pb1, Op<T>::mfma16k(a0, pb0, acc[db] * alpha));
+      }
+
+      const bool run_end = cc.page + c - 1 == cc.R - 1;
+      if (run_end || i + c == n_units) {
+        finish(cstage, cc, run_end);
+        piece_u0 = u_begin + i + c;
+      }
+      cstage = cstage + c >= NST ? cstage + c - NST : cstage + c;
+      if (i + 1 < n_units) advance(cc);
+      if (two && i + 2 < n_units) advance(cc);
+      i += c;
+    }
   }
 }
 

@@ -89,9 +89,10 @@ def test_decode_split_count_invariance():
         assert np.abs(o - outs[0]).max() <= 2e-2
 
 
-def test_named_decode_full():
-    case = CONFIGS["splitkv_decode_bf16_64k"]
-    say(f"decode parity (full size, sampled sequences) {case.name}")
+@pytest.mark.parametrize("d", [128, 64])
+def test_named_decode_full(d):
+    case = CONFIGS["splitkv_decode_bf16_64k"].with_(head_dim=d)
+    say(f"decode parity (full size, sampled sequences) {case.name} d={d}")
     inp = make_decode_inputs(case, seed=0)
     O, _ = gpu_decode(inp, case.num_splits)
     lens = inp.seqlens_k
@@ -103,10 +104,11 @@ def test_named_decode_full():
     assert np.isfinite(O).all()
 
 
-def test_decode_deterministic():
-    case = DecodeCase("det", 4, 32, 8, 128, "bf16", lengths_fixed=(5000, 20000, 64, 1))
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_deterministic(d):
+    case = DecodeCase("det", 4, 32, 8, d, "bf16", lengths_fixed=(5000, 20000, 64, 1))
     inp = make_decode_inputs(case, seed=7)
-    say("decode determinism")
+    say(f"decode determinism d={d}")
     a, _ = gpu_decode(inp, 16)
     b, _ = gpu_decode(inp, 16)
     np.testing.assert_array_equal(a, b)
@@ -198,16 +200,17 @@ def test_decode_large_batch():
         assert np.abs(lse[fin] - lref[fin]).max() <= 1e-3
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("splits", [1, 16])
-def test_decode_invalid_page_ids_are_left_out(splits):
+def test_decode_invalid_page_ids_are_left_out(splits, d):
     import dataclasses
-    case = DecodeCase("bf16_bad_ids", 2, 8, 2, 128, "bf16", lengths_fixed=(1000, 333))
+    case = DecodeCase("bf16_bad_ids", 2, 8, 2, d, "bf16", lengths_fixed=(1000, 333))
     inp = make_decode_inputs(case, seed=15)
     nb = inp.k_cache.shape[0]
     bad = inp.block_table.copy()
     bad[0, 7] = nb + 1
     bad[1, 2] = -5
-    say(f"decode with invalid page ids, num_splits={splits}")
+    say(f"decode with invalid page ids, d={d} num_splits={splits}")
     O, _ = gpu_decode(dataclasses.replace(inp, block_table=bad), splits)
     table = np.zeros_like(inp.block_table)
     keep0 = [j for j in range(16) if j != 7]
