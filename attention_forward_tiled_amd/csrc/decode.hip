@@ -31,7 +31,9 @@
 //     padded to 16 columns as the B operand). The accumulator layout is the B-operand
 //     layout of v_mfma_f32_16x16x16, so O^T += V^T P^T follows with P in registers and
 //     V^T read from the row-major V tile by ds_read_b64_tr_b16. Each wave keeps its own
-//     (m, l, o) per query head; the four are merged through LDS at the end.
+//     (m, l, o) per query head; the four are merged through LDS at the end. The reference
+//     maximum m moves only when a score exceeds it by more than 2^8, so most pages skip
+//     the cross-lane maximum and the rescale.
 //   * Rows past the partition end and rows of pages whose id is out of range are
 //     copied from a block of zeros and their scores are masked, so NaN in unused page
 //     slots never reaches the output.
@@ -60,6 +62,27 @@ __device__ __forceinline__ int dswz(int row) {
     const int r = row & 15;
     return ((r & 7) << 1) | (r >> 3);
   }
+}
+
+// Log2-domain slack before a running reference maximum moves.
+constexpr float kLazy = 8.0f;
+
+// Reference-maximum update of one online-softmax step. m is the row's reference (its
+// denominator and output accumulator are relative to it) and mx this lane's maximum over
+// its new scores. The reference moves to the row maximum only when some score of the wave
+// exceeds m + kLazy; otherwise the cross-lane maximum and the rescale are skipped
+// (alpha = 1) and the new exponentials stay below 2^kLazy. The recurrence holds for any
+// reference, so only rounding changes. Returns the value to exponentiate against.
+__device__ __forceinline__ float move_ref(float& m, float mx, float& alpha) {
+  if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {   // wave-uniform branch
+    const float m_new = fmaxf(m, rows4_max(mx));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    alpha = fast_exp2(m - m_use);
+    m = m_new;
+    return m_use;
+  }
+  alpha = 1.f;
+  return m == -INFINITY ? 0.f : m;
 }
 
 // Wait until at most `ahead` pages of copies (PER wave-instructions each) are still in
@@ -224,11 +247,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
       x[j] = page_ok && key + j < end ? s[j] * p.scale_log2 : -INFINITY;
       mx = fmaxf(mx, x[j]);
     }
-    mx = rows4_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
+    float alpha;
+    const float m_use = move_ref(m, mx, alpha);
     float pr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
@@ -565,11 +585,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
         x[j] = page_ok && key + j < cc.L ? s[j] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, x[j]);
       }
-      mx = rows4_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
+      float alpha;
+      const float m_use = move_ref(m, mx, alpha);
       float pr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
@@ -630,11 +647,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
         x[4 + j] = ok1 && key + kPage + j < cc.L ? s1[j] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, fmaxf(x[j], x[4 + j]));
       }
-      mx = rows4_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
+      float alpha;
+      const float m_use = move_ref(m, mx, alpha);
       float pr[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(x[j] - m_use);
