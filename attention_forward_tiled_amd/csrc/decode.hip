@@ -430,8 +430,12 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
   uint32_t page_ok_bits = 0;   // bit (local unit index mod 32): the page id was valid
 
   // Start the copies of unit `k` (local index) at cursor c into stage `stage`.
-  auto issue = [&](int k, const Cursor& c, int stage) __attribute__((always_inline)) {
-    const int pg = scalar_load(p.block_table + (int64_t)c.b * p.max_blocks + c.page);
+  // Page id of the unit at cursor c; read one issue ahead of its use so that the scalar
+  // load's wait is not on the path from a barrier to the next copies.
+  auto page_id = [&](const Cursor& c) __attribute__((always_inline)) {
+    return scalar_load(p.block_table + (int64_t)c.b * p.max_blocks + c.page);
+  };
+  auto issue = [&](int k, const Cursor& c, int stage, int pg) __attribute__((always_inline)) {
     const bool page_ok = pg >= 0 && pg < p.num_blocks;
     page_ok_bits = (page_ok_bits & ~(1u << (k & 31))) | ((uint32_t)page_ok << (k & 31));
     const int64_t base = (int64_t)(page_ok ? pg : 0) * kPage * rs + (int64_t)kvh * D;
@@ -487,15 +491,19 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
 
   const int b_first = scalar_load(p.start + jr);
   Cursor ic = cursor_at(b_first, u_begin);   // next unit to copy
+  int ipg = page_id(ic);                     // its page id
   Cursor cc = ic;                            // unit being consumed
   int piece_u0 = u_begin;                    // first unit of the current partition
 
   int istage = 0;
   const int pro = min(NST - 1, n_units);
   for (int k = 0; k < pro; ++k) {
-    issue(k, ic, istage);
+    issue(k, ic, istage, ipg);
     istage = istage + 1 == NST ? 0 : istage + 1;
-    if (k + 1 < n_units) advance(ic);
+    if (k + 1 < n_units) {
+      advance(ic);
+      ipg = page_id(ic);
+    }
   }
 
   // End of a partition whose last unit sits in `stage` (consumed by every wave): merge the
@@ -564,9 +572,12 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
       wait_pages<PER, NST - 2>(min(NST - 2, n_units - 1 - i));
       __syncthreads();   // unit i visible to every wave; the stage of unit i - 1 is free
       if (i + NST - 1 < n_units) {
-        issue(i + NST - 1, ic, istage);
+        issue(i + NST - 1, ic, istage, ipg);
         istage = istage + 1 == NST ? 0 : istage + 1;
-        if (i + NST < n_units) advance(ic);
+        if (i + NST < n_units) {
+          advance(ic);
+          ipg = page_id(ic);
+        }
       }
 
       const char* st = ring + cstage * STAGE_B;
@@ -621,9 +632,12 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
 #pragma unroll
       for (int r = 0; r < 2; ++r)
         if (issued < n_units && issued - i < NST) {
-          issue(issued, ic, istage);
+          issue(issued, ic, istage, ipg);
           istage = istage + 1 == NST ? 0 : istage + 1;
-          if (++issued < n_units) advance(ic);
+          if (++issued < n_units) {
+            advance(ic);
+            ipg = page_id(ic);
+          }
         }
 
       const char* sa = ring + cstage * STAGE_B;
