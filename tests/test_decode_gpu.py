@@ -224,3 +224,30 @@ def test_decode_invalid_page_ids_are_left_out(splits, d):
     ref = dataclasses.replace(inp, block_table=table, seqlens_k=np.array([1000 - 64, 333 - 64], dtype=np.int32))
     Oref, _ = oracle_decode(ref)
     assert max_abs_err(O, Oref) <= TOL[case.dtype]
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_growing_scores(d):
+    # keys scaled up along each sequence (up to 12x at its end), so later pages keep
+    # raising each row's maximum, at first by far more than 2^8 per page and later by
+    # small steps: both the moves of the running reference and the pages that keep it
+    # are exercised against the exact softmax
+    import dataclasses
+    from attn_workloads.generate import bits_to_f32, round_to_bits
+    case = DecodeCase("bf16_ramp", 3, 8, 2, d, "bf16", lengths_fixed=(2000, 700, 4000))
+    inp = make_decode_inputs(case, seed=21)
+    k = bits_to_f32(inp.k_cache, "bf16")
+    for b, L in enumerate(inp.seqlens_k.tolist()):
+        for t in range(0, L, 64):
+            n = min(64, L - t)
+            ramp = 0.25 + 12.0 * ((t + np.arange(n)) / L) ** 2
+            k[inp.block_table[b, t // 64], :n] *= ramp[:, None, None].astype(np.float32)
+    grown = dataclasses.replace(inp, k_cache=round_to_bits(k, "bf16"))
+    Oref, lref = oracle_decode(grown)
+    for s in (1, 3, 16):
+        say(f"decode growing scores d={d} num_splits={s}")
+        O, lse = gpu_decode(grown, s, with_lse=True)
+        err = max_abs_err(O, Oref)
+        say(f"  max abs err {err:.3e}, lse err {np.abs(lse - lref).max():.3e}")
+        assert err <= TOL[case.dtype]
+        assert np.abs(lse - lref).max() <= 1e-3
