@@ -300,3 +300,40 @@ def test_prefill_invalid_page_ids_are_left_out(case):
     lens[:2] -= 64
     Oref, _ = oracle_prefill(dataclasses.replace(inp, block_table=table, seqlens_k=lens))
     assert max_abs_err(O, Oref) <= tolerance(case)
+
+
+# Keys scaled up along the sequence (up to 12x at its end): along a row's key tiles the
+# maximum keeps rising, at first by far more than 2^8 per tile and later by small steps,
+# so the lazily moved reference maximum, its per-lane check and the skipped rescales all
+# meet the exact softmax. One case per launch form.
+GROWING = [
+    P("bf16_d128_gqa4_causal_growing_pairs", 1, 32, 8, 2048, 2048, 128, "bf16", True, "dense"),
+    P("f16_d128_gqa4_causal_growing_two_groups", 1, 8, 2, 1000, 1000, 128, "f16", True, "dense"),
+    P("bf16_d64_noncausal_growing_wg4", 2, 8, 2, 700, 900, 64, "bf16", False, "dense"),
+    P("bf16_d128_noncausal_growing_wg8", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense"),
+]
+
+
+@pytest.mark.parametrize("case", GROWING, ids=lambda c: c.name)
+def test_prefill_growing_scores(case):
+    import dataclasses
+    from attn_workloads.generate import bits_to_f32, round_to_bits
+    say(f"prefill growing scores {case}")
+    inp = make_prefill_inputs(case, seed=23)
+    ramp = (0.25 + 12.0 * (np.arange(case.seqlen_k) / case.seqlen_k) ** 2).astype(np.float32)
+    k = bits_to_f32(inp.k, case.dtype) * ramp[None, :, None, None]
+    grown = dataclasses.replace(inp, k=round_to_bits(k, case.dtype))
+    O, lse = gpu_prefill(grown, with_lse=True)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, case.seqlen_q - 1],
+                                     np.random.default_rng(2).choice(case.seqlen_q, 40, replace=False)]))
+    rows = rows[rows < case.seqlen_q]
+    Oref, lref = oracle_prefill(grown, q_index=rows)
+    err = max_abs_err(O[:, rows], Oref)
+    lerr = np.abs(lse[:, :, rows] - lref).max()
+    say(f"  max abs err {err:.3e}, lse err {lerr:.3e} over {rows.size} rows x all (b, h)")
+    assert err <= tolerance(case)
+    # l is summed from P as rounded to the 16-bit type the P.V product consumes (so the
+    # output's weights sum to one); where one key dominates a row, that term's rounding
+    # (relative <= the unit roundoff u: 2^-8 bf16, 2^-11 fp16) reaches lse unaveraged
+    u = 2.0 ** -8 if case.dtype == "bf16" else 2.0 ** -11
+    assert lerr <= max(1e-3, 1.05 * u)
