@@ -170,3 +170,16 @@ def test_missing_library_raises(tmp_path, monkeypatch):
     from attention_forward_tiled_amd import attn_decode_workspace_bytes
     with pytest.raises(RuntimeError, match="not built"):
         attn_decode_workspace_bytes(1, 4, 2, 64)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU only: a request for several exits non-zero with a message, before any
+    # device work
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2", "--steps", "1"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in (r.stdout + r.stderr)
+    assert r.stdout.strip() == "" or not r.stdout.lstrip().startswith("{")
