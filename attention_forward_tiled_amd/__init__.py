@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     AttnError,
     attn_decode_fwd,
     attn_decode_workspace_bytes,
+    attn_device_info,
     attn_prefill_fwd,
     attn_splitkv_combine,
 )

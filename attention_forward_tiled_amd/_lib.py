@@ -18,10 +18,11 @@ ATTN_BSHD, ATTN_BHSD = 0, 1
 ATTN_ROUND_RTNE, ATTN_ROUND_RTNA, ATTN_ROUND_RTZ = 0, 1, 2
 ATTN_PAGE_SIZE = 64
 ATTN_MAX_SPLITS = 64
-ATTN_ABI_VERSION = 3
+ATTN_ABI_VERSION = 4
 
 EXPORTS = ("attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes",
-           "attn_splitkv_combine", "attn_last_error", "attn_abi_version", "attn_device_count")
+           "attn_splitkv_combine", "attn_last_error", "attn_abi_version", "attn_device_count",
+           "attn_device_info")
 
 _c_void_p, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -53,6 +54,13 @@ class CombineArgs(ctypes.Structure):
                 ("head_dim", _i32), ("o_dtype", _i32), ("o_round", _i32)]
 
 
+class DeviceInfo(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 256), ("arch", ctypes.c_char * 256),
+                ("total_memory", ctypes.c_int64), ("compute_units", _i32), ("clock_khz", _i32),
+                ("memory_clock_khz", _i32), ("memory_bus_bits", _i32), ("lds_per_cu", _i32),
+                ("l2_bytes", _i32), ("runtime_version", _i32), ("driver_version", _i32)]
+
+
 _LIB = None
 
 
@@ -80,6 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_abi_version.restype = _i32
     lib.attn_device_count.argtypes = []
     lib.attn_device_count.restype = _i32
+    lib.attn_device_info.argtypes = [_i32, ctypes.POINTER(DeviceInfo)]
+    lib.attn_device_info.restype = ctypes.c_int
     if lib.attn_abi_version() != ATTN_ABI_VERSION:
         raise RuntimeError(f"libattn.so ABI version {lib.attn_abi_version()} != {ATTN_ABI_VERSION}")
     _LIB = lib

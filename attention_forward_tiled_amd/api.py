@@ -7,7 +7,6 @@ Shapes are read from the tensors; the library re-validates everything.
 from __future__ import annotations
 
 import ctypes
-import math
 from typing import Optional
 
 import torch
@@ -180,5 +179,9 @@ def attn_splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, *,
     return out
 
 
-def default_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)
+def attn_device_info(device: int = 0) -> dict:
+    """Facts of HIP device ``device`` as the library reads them (attn_device_info)."""
+    info = _lib.DeviceInfo()
+    _check(_lib.load().attn_device_info(int(device), ctypes.byref(info)))
+    return {f: (getattr(info, f).decode(errors="replace") if f in ("name", "arch") else int(getattr(info, f)))
+            for f, _ in _lib.DeviceInfo._fields_}

@@ -98,6 +98,37 @@ int32_t attn_device_count(void) {
   return n;
 }
 
+attn_status_t attn_device_info(int32_t device, attn_device_info_t* info) {
+  try {
+    if (!info) return fail(ATTN_ERR_INVALID_ARG, "info is NULL");
+    if (device < 0) return fail(ATTN_ERR_INVALID_ARG, "device must be >= 0 (got %d)", device);
+    if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
+    const int n = attn_device_count();
+    if (device >= n) return fail(ATTN_ERR_INVALID_ARG, "device %d is not visible (%d device(s))", device, n);
+    hipDeviceProp_t prop{};
+    if (hipError_t e = hipGetDeviceProperties(&prop, device); e != hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    *info = attn_device_info_t{};
+    snprintf(info->name, sizeof(info->name), "%s", prop.name);
+    snprintf(info->arch, sizeof(info->arch), "%s", prop.gcnArchName);
+    info->total_memory = (int64_t)prop.totalGlobalMem;
+    info->compute_units = prop.multiProcessorCount;
+    info->clock_khz = prop.clockRate;
+    info->memory_clock_khz = prop.memoryClockRate;
+    info->memory_bus_bits = prop.memoryBusWidth;
+    info->lds_per_cu = (int32_t)prop.maxSharedMemoryPerMultiProcessor;
+    info->l2_bytes = prop.l2CacheSize;
+    int rv = 0, dv = 0;
+    if (hipRuntimeGetVersion(&rv) != hipSuccess) rv = 0;
+    if (hipDriverGetVersion(&dv) != hipSuccess) dv = 0;
+    info->runtime_version = rv;
+    info->driver_version = dv;
+    return ok();
+  } catch (...) {
+    return fail(ATTN_ERR_LAUNCH, "internal error in attn_device_info");
+  }
+}
+
 attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
   try {
     if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");

@@ -33,7 +33,9 @@
 //     V^T read from the row-major V tile by ds_read_b64_tr_b16. Each wave keeps its own
 //     (m, l, o) per query head; the four are merged through LDS at the end. The reference
 //     maximum m moves only when a score exceeds it by more than 2^8, so most pages skip
-//     the cross-lane maximum and the rescale.
+//     the cross-lane maximum and the rescale. The denominator l sums P as rounded to the
+//     16-bit type for the P.V product (v_dot2 on the packed values), as the prefill does,
+//     so each partial output is a weighted mean of V rows whose weights sum to one.
 //   * Rows past the partition end and rows of pages whose id is out of range are
 //     copied from a block of zeros and their scores are masked, so NaN in unused page
 //     slots never reaches the output.
@@ -252,8 +254,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
     float pr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     const u32x2 pb = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
+    lsum = Op<T>::sum2(pb[1], Op<T>::sum2(pb[0], lsum * alpha));
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const u32x2 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(vt + voff[db]));
@@ -601,8 +603,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
       float pr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_use);
-      lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
       const u32x2 pb = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
+      lsum = Op<T>::sum2(pb[1], Op<T>::sum2(pb[0], lsum * alpha));
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const u32x2 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(st + voff[db]));
@@ -666,9 +668,9 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
       float pr[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(x[j] - m_use);
-      lsum = lsum * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
       const u32x2 pb0 = u32x2{pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3])};
       const u32x2 pb1 = u32x2{pack2<T>(pr[4], pr[5]), pack2<T>(pr[6], pr[7])};
+      lsum = Op<T>::sum2(pb1[1], Op<T>::sum2(pb1[0], Op<T>::sum2(pb0[1], Op<T>::sum2(pb0[0], lsum * alpha))));
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const u32x2 a0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(sa + voff[db]));

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 #define ATTN_PAGE_SIZE 64      /* tokens per KV page (block_size); equal to the KV tile width */
 #define ATTN_MAX_SPLITS 64     /* upper bound of num_splits for the split-KV decode */
 
@@ -243,6 +243,29 @@ int32_t attn_abi_version(void);
 
 /* Number of visible HIP devices (0 when none or when the runtime is unavailable). */
 int32_t attn_device_count(void);
+
+/* Facts of one HIP device, read from hipDeviceProp_t and the runtime, so that measured
+ * throughput can be stated against peaks derived from the device itself (matrix-core
+ * peak = compute units x engine clock x flops per clock and CU). Strings are
+ * NUL-terminated and truncated to their buffers. */
+typedef struct {
+  char name[256];              /* marketing name */
+  char arch[256];              /* gcnArchName, e.g. "gfx950:sramecc+:xnack-" */
+  int64_t total_memory;        /* bytes of device memory */
+  int32_t compute_units;       /* multiProcessorCount */
+  int32_t clock_khz;           /* clockRate: peak engine clock */
+  int32_t memory_clock_khz;    /* memoryClockRate */
+  int32_t memory_bus_bits;     /* memoryBusWidth */
+  int32_t lds_per_cu;          /* maxSharedMemoryPerMultiProcessor, bytes */
+  int32_t l2_bytes;            /* l2CacheSize */
+  int32_t runtime_version;     /* hipRuntimeGetVersion */
+  int32_t driver_version;      /* hipDriverGetVersion */
+} attn_device_info_t;
+
+/* Fill *info for HIP device `device`. Errors: INVALID_ARG for a NULL info or a device
+ * index outside [0, attn_device_count()), NO_DEVICE when no device is visible, LAUNCH
+ * when the runtime refuses the query. */
+attn_status_t attn_device_info(int32_t device, attn_device_info_t* info);
 
 #ifdef __cplusplus
 }

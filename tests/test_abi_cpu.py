@@ -44,6 +44,7 @@ def test_struct_sizes():
     assert ctypes.sizeof(_lib.PrefillArgs) == 8 * 8 + 15 * 4 + 4      # tail padding to 8
     assert ctypes.sizeof(_lib.DecodeArgs) == 8 * 8 + 8 + 12 * 4
     assert ctypes.sizeof(_lib.CombineArgs) == 4 * 8 + 6 * 4
+    assert ctypes.sizeof(_lib.DeviceInfo) == 2 * 256 + 8 + 8 * 4
 
 
 FAKE = 0x1000  # aligned non-null pointer value; never dereferenced (validation fails first)
@@ -107,6 +108,14 @@ def test_null_args_pointer(lib):
     assert lib.attn_prefill_fwd(None, None) == _lib.ATTN_ERR_INVALID_ARG
     assert lib.attn_decode_fwd(None, None) == _lib.ATTN_ERR_INVALID_ARG
     assert lib.attn_splitkv_combine(None, None) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_device_info(0, None) == _lib.ATTN_ERR_INVALID_ARG
+    assert "NULL" in _lib.last_error()
+
+
+def test_device_info_rejects_negative_index(lib):
+    info = _lib.DeviceInfo()
+    assert lib.attn_device_info(-1, ctypes.byref(info)) == _lib.ATTN_ERR_INVALID_ARG
+    assert "device" in _lib.last_error()
 
 
 def test_prefill_empty_is_noop(lib):
@@ -157,6 +166,7 @@ def test_valid_call_without_device_reports_no_device(lib):
     assert lib.attn_prefill_fwd(ctypes.byref(prefill_args()), None) == _lib.ATTN_ERR_NO_DEVICE
     assert lib.attn_decode_fwd(ctypes.byref(decode_args()), None) == _lib.ATTN_ERR_NO_DEVICE
     assert lib.attn_splitkv_combine(ctypes.byref(combine_args()), None) == _lib.ATTN_ERR_NO_DEVICE
+    assert lib.attn_device_info(0, ctypes.byref(_lib.DeviceInfo())) == _lib.ATTN_ERR_NO_DEVICE
 
 
 def test_missing_library_raises(tmp_path, monkeypatch):

@@ -6,7 +6,8 @@ import torch
 
 import oracle
 from attn_workloads import CONFIGS, DecodeCase, make_decode_inputs
-from gpu_util import TOL, check_bf16_rounding, dev, dev_i32, max_abs_err, oracle_decode, say, to_f64
+from gpu_util import (TOL, check_bf16_rounding, dev, dev_i32, lse_tolerance, max_abs_err, oracle_decode, say,
+                      to_f64)
 from oracle.rounding import round_bf16
 
 pytestmark = [pytest.mark.gpu,
@@ -14,14 +15,22 @@ pytestmark = [pytest.mark.gpu,
 
 
 def gpu_decode(inp, num_splits, out_dtype=None, with_lse=False, out_round="rtne"):
+    """attn_decode_fwd on the seeded inputs. The output and lse buffers are NaN-filled
+    before the call and must come back written (O finite, lse never NaN)."""
     from attention_forward_tiled_amd import attn_decode_fwd
     c = inp.case
     lse = torch.full((c.batch, c.heads_q), float("nan"), device="cuda") if with_lse else None
+    out = torch.full((c.batch, c.heads_q, c.head_dim), float("nan"),
+                     dtype={"bf16": torch.bfloat16, "f16": torch.float16}[c.dtype] if out_dtype is None
+                     else out_dtype, device="cuda")
     o = attn_decode_fwd(dev(inp.q, c.dtype), dev(inp.k_cache, c.dtype), dev(inp.v_cache, c.dtype),
                         dev_i32(inp.block_table), dev_i32(inp.seqlens_k),
                         max_seqlen_k=inp.max_seqlen_k, num_splits=num_splits,
-                        out_dtype=out_dtype, lse=lse, out_round=out_round)
+                        out=out, lse=lse, out_round=out_round)
     torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()), "decode output left unwritten (NaN) or non-finite"
+    if lse is not None:
+        assert not bool(torch.isnan(lse).any()), "decode lse left unwritten"
     return to_f64(o), (to_f64(lse) if with_lse else None)
 
 
@@ -47,7 +56,7 @@ def test_decode_small(case, splits):
         err = max_abs_err(O, Oref)
         say(f"  max abs err {err:.3e}")
         assert err <= TOL[case.dtype]
-        assert np.abs(lse - lref).max() <= 1e-3
+        assert np.abs(lse - lref).max() <= lse_tolerance(case.dtype)
 
 
 @pytest.mark.parametrize("d", [128, 64])
@@ -63,7 +72,7 @@ def test_decode_empty_sequences(splits, d):
     assert max_abs_err(O, Oref) <= TOL[case.dtype]
     empty = inp.seqlens_k == 0
     assert (O[empty] == 0).all() and np.isneginf(lse[empty]).all() and np.isneginf(lref[empty]).all()
-    assert np.abs(lse[~empty] - lref[~empty]).max() <= 1e-3
+    assert np.abs(lse[~empty] - lref[~empty]).max() <= lse_tolerance(case.dtype)
 
 
 def test_decode_many_short_sequences():
@@ -76,7 +85,7 @@ def test_decode_many_short_sequences():
         say(f"decode many short sequences num_splits={s}")
         O, lse = gpu_decode(inp, s, with_lse=True)
         assert max_abs_err(O, Oref) <= TOL[case.dtype]
-        assert np.abs(lse - lref).max() <= 1e-3
+        assert np.abs(lse - lref).max() <= lse_tolerance(case.dtype)
 
 
 @pytest.mark.parametrize("d", [128, 64])
@@ -95,17 +104,19 @@ def test_decode_split_count_invariance(d):
 
 @pytest.mark.parametrize("d", [128, 64])
 def test_named_decode_full(d):
+    # Full size, every sequence and head against the oracle (run one sequence at a time
+    # to bound host memory), in the launch configuration the benchmark times.
     case = CONFIGS["splitkv_decode_bf16_64k"].with_(head_dim=d)
-    say(f"decode parity (full size, sampled sequences) {case.name} d={d}")
+    say(f"decode parity (full size, all sequences) {case.name} d={d}")
     inp = make_decode_inputs(case, seed=0)
-    O, _ = gpu_decode(inp, case.num_splits)
-    lens = inp.seqlens_k
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, case.batch - 1})
-    Oref, _ = oracle_decode(inp, pick)
-    err = max_abs_err(O[pick], Oref)
-    say(f"  max abs err {err:.3e} over sequences {pick} (lengths {lens[pick].tolist()})")
+    O, lse = gpu_decode(inp, case.num_splits, with_lse=True)
+    Oref, lref = oracle_decode(inp, per_call=1)
+    err = max_abs_err(O, Oref)
+    lerr = float(np.abs(lse - lref).max())
+    say(f"  max abs err {err:.3e}, lse err {lerr:.3e} over all {case.batch} sequences "
+        f"(lengths {int(inp.seqlens_k.min())}..{int(inp.seqlens_k.max())})")
     assert err <= TOL[case.dtype]
-    assert np.isfinite(O).all()
+    assert lerr <= lse_tolerance(case.dtype)
 
 
 @pytest.mark.parametrize("d", [128, 64])
@@ -186,7 +197,7 @@ def test_decode_long_context():
         say(f"decode long context num_splits={s}")
         O, lse = gpu_decode(inp, s, with_lse=True)
         assert max_abs_err(O, Oref) <= TOL[case.dtype]
-        assert np.abs(lse - lref).max() <= 1e-3
+        assert np.abs(lse - lref).max() <= lse_tolerance(case.dtype)
 
 
 def test_decode_large_batch():
@@ -201,7 +212,7 @@ def test_decode_large_batch():
         assert max_abs_err(O, Oref) <= TOL[case.dtype]
         fin = np.isfinite(lref)
         assert (np.isneginf(lse) == ~fin).all()
-        assert np.abs(lse[fin] - lref[fin]).max() <= 1e-3
+        assert np.abs(lse[fin] - lref[fin]).max() <= lse_tolerance(case.dtype)
 
 
 @pytest.mark.parametrize("d", [128, 64])
@@ -250,4 +261,4 @@ def test_decode_growing_scores(d):
         err = max_abs_err(O, Oref)
         say(f"  max abs err {err:.3e}, lse err {np.abs(lse - lref).max():.3e}")
         assert err <= TOL[case.dtype]
-        assert np.abs(lse - lref).max() <= 1e-3
+        assert np.abs(lse - lref).max() <= lse_tolerance(case.dtype)
