@@ -10,6 +10,7 @@ every entry point loads the library on first use and raises if it is not built
 from .api import (  # noqa: F401
     AttnError,
     attn_decode_fwd,
+    attn_decode_fwd_noalloc,
     attn_decode_workspace_bytes,
     attn_device_info,
     attn_prefill_fwd,

@@ -18,11 +18,12 @@ ATTN_BSHD, ATTN_BHSD = 0, 1
 ATTN_ROUND_RTNE, ATTN_ROUND_RTNA, ATTN_ROUND_RTZ = 0, 1, 2
 ATTN_PAGE_SIZE = 64
 ATTN_MAX_SPLITS = 64
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 ATTN_ABI_VERSION = 4
 
 EXPORTS = ("attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes",
            "attn_splitkv_combine", "attn_last_error", "attn_abi_version", "attn_device_count",
-           "attn_device_info")
+           "attn_device_info", "attn_decode_fwd_noalloc")
 
 _c_void_p, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -78,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_prefill_fwd.restype = ctypes.c_int
     lib.attn_decode_fwd.argtypes = [ctypes.POINTER(DecodeArgs), _c_void_p]
     lib.attn_decode_fwd.restype = ctypes.c_int
+    lib.attn_decode_fwd_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _c_void_p]
+    lib.attn_decode_fwd_noalloc.restype = ctypes.c_int
     lib.attn_splitkv_combine.argtypes = [ctypes.POINTER(CombineArgs), _c_void_p]
     lib.attn_splitkv_combine.restype = ctypes.c_int
     lib.attn_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]

@@ -163,6 +163,34 @@ def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     return out
 
 
+def attn_decode_fwd_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_table: torch.Tensor, seqlens_k: torch.Tensor, *, max_seqlen_k: int,
+                            num_splits: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                            scale: float = 0.0, out_round: str = "rtne", stream=None) -> torch.Tensor:
+    """Split-KV decode without a workspace (the library's static device scratch).
+
+    Same arguments as attn_decode_fwd, but ``out`` must be passed (this call allocates
+    nothing, here or in the library). Calls that overlap on one device race on the
+    shared scratch; calls ordered on one stream do not."""
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    _need(k_cache, "k_cache", (q.dtype,))
+    _need(v_cache, "v_cache", (q.dtype,))
+    _need(block_table, "block_table", (torch.int32,))
+    _need(seqlens_k, "seqlens_k", (torch.int32,))
+    _need(out, "out", tuple(_DT))
+    num_blocks, page, Hkv, d = k_cache.shape
+    if page != _lib.ATTN_PAGE_SIZE:
+        raise ValueError(f"pages must hold {_lib.ATTN_PAGE_SIZE} tokens")
+    B = block_table.shape[0]
+    Hq = q.numel() // (B * d) if B else 0
+    a = _lib.DecodeArgs(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
+        _ptr(lse), None, 0, B, Hq, Hkv, d, num_blocks, block_table.shape[1], int(max_seqlen_k),
+        int(num_splits), _DT[q.dtype], _DT[out.dtype], float(scale), _round(out_round))
+    _check(_lib.load().attn_decode_fwd_noalloc(ctypes.byref(a), _stream(stream)))
+    return out
+
+
 def attn_splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, *,
                          out: Optional[torch.Tensor] = None, out_dtype=torch.float32,
                          lse: Optional[torch.Tensor] = None, out_round: str = "rtne",

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/attn.h"
@@ -80,6 +81,165 @@ int device_cus() {
   if (dev < 64) cache[dev] = n;
   return n;
 }
+
+}  // namespace
+
+namespace {
+
+// ---- scratch of the allocation-free decode (attn_decode_fwd_noalloc)
+//
+// The split partials and the partition plan of a decode go to this file-scope device
+// array instead of a caller workspace. Each device the library runs on holds its own copy
+// until the process ends. In host code the array's name is only a host-side stand-in:
+// its device address is looked up once per device, with that device current, and only
+// that address is ever passed to kernels.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+attn_status_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_NO_DEVICE, "no current HIP device");
+  }
+  if (dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(ATTN_ERR_LAUNCH, "hipGetSymbolAddress of the decode scratch failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return ATTN_OK;
+}
+
+// The decode of attn_decode_fwd and attn_decode_fwd_noalloc: the caller's workspace, or
+// (noalloc) this device's copy of the static scratch array.
+attn_status_t decode_impl(const attn_decode_args_t* a, void* stream, bool noalloc) {
+  const char* fn = noalloc ? "attn_decode_fwd_noalloc" : "attn_decode_fwd";
+  try {
+    if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+    if (a->batch < 0) return fail(ATTN_ERR_INVALID_ARG, "batch must be >= 0");
+    if (a->qkv_dtype != ATTN_F16 && a->qkv_dtype != ATTN_BF16)
+      return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
+    if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
+      return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+    if (attn_status_t st = check_round(a->o_round, a->o_dtype); st != ATTN_OK) return st;
+    if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
+    if (a->num_heads_q <= 0 || a->num_heads_kv <= 0)
+      return fail(ATTN_ERR_INVALID_ARG, "head counts must be positive");
+    if (a->num_heads_q % a->num_heads_kv != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
+                  a->num_heads_q, a->num_heads_kv);
+    const int G = a->num_heads_q / a->num_heads_kv;
+    if (G > 16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports GQA ratios up to 16 (got %d)", G);
+    if (a->num_splits < 1 || a->num_splits > ATTN_MAX_SPLITS)
+      return fail(ATTN_ERR_INVALID_ARG, "num_splits must be in [1, %d]", ATTN_MAX_SPLITS);
+    if (a->max_seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_k must be >= 0");
+    if (a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
+      return fail(ATTN_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be positive");
+    if ((int64_t)a->max_blocks_per_seq * ATTN_PAGE_SIZE < a->max_seqlen_k)
+      return fail(ATTN_ERR_INVALID_ARG, "block table holds %lld keys, fewer than max_seqlen_k = %d",
+                  (long long)a->max_blocks_per_seq * ATTN_PAGE_SIZE, a->max_seqlen_k);
+    if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    if (a->batch > kMaxGridYZ || a->num_heads_kv > kMaxGridYZ)
+      return fail(ATTN_ERR_UNSUPPORTED, "batch and num_heads_kv must be <= %lld", (long long)kMaxGridYZ);
+    if (a->batch == 0) return ok();
+    if (!a->q || !a->k_cache || !a->v_cache || !a->o || !a->block_table || !a->seqlens_k)
+      return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seqlens_k, o%s must be non-NULL",
+                  noalloc ? "" : " and workspace");
+    if (!noalloc && !a->workspace)
+      return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seqlens_k, o and workspace must be non-NULL");
+    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned4(a->o))
+      return fail(ATTN_ERR_INVALID_ARG, "q, k_cache and v_cache must be 16-byte aligned, o 4-byte aligned");
+    if (!aligned4(a->block_table) || !aligned4(a->seqlens_k) || (a->lse && !aligned4(a->lse)))
+      return fail(ATTN_ERR_INVALID_ARG, "block_table, seqlens_k and lse must be 4-byte aligned");
+    const size_t need = attn_decode_workspace_bytes(a->batch, a->num_heads_q, a->num_splits, a->head_dim);
+    if (noalloc) {
+      if (a->workspace || a->workspace_bytes)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode_fwd_noalloc takes no workspace (pass NULL and 0 bytes)");
+      if (need > ATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "this decode needs %zu bytes of scratch, above the %zu-byte maximum of "
+                    "attn_decode_fwd_noalloc (use attn_decode_fwd with a workspace)",
+                    need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+    } else {
+      if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+      if (a->workspace_bytes < need)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace has %zu bytes, needs %zu", a->workspace_bytes, need);
+    }
+
+    if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
+    void* wsp = a->workspace;
+    if (noalloc) {
+      if (attn_status_t st = scratch_address(&wsp); st != ATTN_OK) return st;
+    }
+    const int64_t rows = (int64_t)a->batch * a->num_heads_q * a->num_splits;
+    char* ws = static_cast<char*>(wsp);
+    float* part_o = reinterpret_cast<float*>(ws);
+    const size_t lse_off = align256((size_t)rows * a->head_dim * sizeof(float));
+    float* part_lse = reinterpret_cast<float*>(ws + lse_off);
+    const size_t plan_off = lse_off + align256((size_t)rows * sizeof(float));
+    int32_t* plan = reinterpret_cast<int32_t*>(ws + plan_off);
+    int32_t* prefix = reinterpret_cast<int32_t*>(ws + plan_off + 256);
+    int32_t* start = reinterpret_cast<int32_t*>(ws + plan_off + 256 +
+                                                align256((size_t)(a->batch + 1) * sizeof(int32_t)));
+    int part = (a->max_seqlen_k + a->num_splits - 1) / a->num_splits;
+    part = ((part + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE) * ATTN_PAGE_SIZE;
+    if (part == 0) part = ATTN_PAGE_SIZE;
+
+    attn::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(a->q);
+    p.k = static_cast<const uint16_t*>(a->k_cache);
+    p.v = static_cast<const uint16_t*>(a->v_cache);
+    p.block_table = a->block_table; p.seqlens_k = a->seqlens_k;
+    p.part_o = part_o; p.part_lse = part_lse;
+    p.batch = a->batch; p.hq = a->num_heads_q; p.hkv = a->num_heads_kv; p.group = G;
+    p.num_blocks = a->num_blocks; p.max_blocks = a->max_blocks_per_seq;
+    p.max_seqlen_k = a->max_seqlen_k; p.num_splits = a->num_splits; p.part_tokens = part;
+    const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+
+    p.plan = plan; p.prefix = prefix; p.start = start;
+
+    attn::CombineParams c{};
+    c.part_o = part_o; c.part_lse = part_lse; c.o = a->o; c.lse = a->lse;
+    c.pairs = a->batch * a->num_heads_q; c.num_splits = a->num_splits; c.o_dtype = a->o_dtype;
+    c.o_round = a->o_dtype == ATTN_BF16 ? a->o_round : 0;
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // Balanced split kernel when partitions may be cut (num_splits >= 2) and the page
+    // count per KV head fits in int32; otherwise one workgroup per fixed partition.
+    const int64_t rmax = ((int64_t)a->max_seqlen_k + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE;
+    const int cus = device_cus();
+    if (a->num_splits >= 2 && (int64_t)a->batch * rmax < (int64_t(1) << 30) && cus > 0) {
+      p.nwk = std::max(1, std::min(kMaxStreamWG, cus / a->num_heads_kv));
+      c.seqlens_k = a->seqlens_k; c.heads = a->num_heads_q; c.max_seqlen_k = a->max_seqlen_k;
+      if (attn_status_t st = launch_status(attn::launch_decode_stream(p, a->head_dim, a->qkv_dtype, s),
+                                           "decode split");
+          st != ATTN_OK)
+        return st;
+    } else if (attn_status_t st = launch_status(attn::launch_decode_split(p, a->head_dim, a->qkv_dtype, s),
+                                                "decode split");
+               st != ATTN_OK) {
+      return st;
+    }
+    return launch_status(attn::launch_combine(c, a->head_dim, s), "decode combine");
+  } catch (...) {
+    return fail(ATTN_ERR_LAUNCH, "internal error in %s", fn);
+  }
+}
+
 
 }  // namespace
 
@@ -252,101 +412,11 @@ attn_status_t attn_splitkv_combine(const attn_combine_args_t* a, void* stream) {
 }
 
 attn_status_t attn_decode_fwd(const attn_decode_args_t* a, void* stream) {
-  try {
-    if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
-    if (a->batch < 0) return fail(ATTN_ERR_INVALID_ARG, "batch must be >= 0");
-    if (a->qkv_dtype != ATTN_F16 && a->qkv_dtype != ATTN_BF16)
-      return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
-    if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
-      return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
-    if (attn_status_t st = check_round(a->o_round, a->o_dtype); st != ATTN_OK) return st;
-    if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
-    if (a->num_heads_q <= 0 || a->num_heads_kv <= 0)
-      return fail(ATTN_ERR_INVALID_ARG, "head counts must be positive");
-    if (a->num_heads_q % a->num_heads_kv != 0)
-      return fail(ATTN_ERR_INVALID_ARG, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
-                  a->num_heads_q, a->num_heads_kv);
-    const int G = a->num_heads_q / a->num_heads_kv;
-    if (G > 16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports GQA ratios up to 16 (got %d)", G);
-    if (a->num_splits < 1 || a->num_splits > ATTN_MAX_SPLITS)
-      return fail(ATTN_ERR_INVALID_ARG, "num_splits must be in [1, %d]", ATTN_MAX_SPLITS);
-    if (a->max_seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_k must be >= 0");
-    if (a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
-      return fail(ATTN_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be positive");
-    if ((int64_t)a->max_blocks_per_seq * ATTN_PAGE_SIZE < a->max_seqlen_k)
-      return fail(ATTN_ERR_INVALID_ARG, "block table holds %lld keys, fewer than max_seqlen_k = %d",
-                  (long long)a->max_blocks_per_seq * ATTN_PAGE_SIZE, a->max_seqlen_k);
-    if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
-    if (a->batch > kMaxGridYZ || a->num_heads_kv > kMaxGridYZ)
-      return fail(ATTN_ERR_UNSUPPORTED, "batch and num_heads_kv must be <= %lld", (long long)kMaxGridYZ);
-    if (a->batch == 0) return ok();
-    if (!a->q || !a->k_cache || !a->v_cache || !a->o || !a->block_table || !a->seqlens_k || !a->workspace)
-      return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seqlens_k, o and workspace must be non-NULL");
-    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned4(a->o))
-      return fail(ATTN_ERR_INVALID_ARG, "q, k_cache and v_cache must be 16-byte aligned, o 4-byte aligned");
-    if (!aligned4(a->block_table) || !aligned4(a->seqlens_k) || (a->lse && !aligned4(a->lse)))
-      return fail(ATTN_ERR_INVALID_ARG, "block_table, seqlens_k and lse must be 4-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
-      return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    const size_t need = attn_decode_workspace_bytes(a->batch, a->num_heads_q, a->num_splits, a->head_dim);
-    if (a->workspace_bytes < need)
-      return fail(ATTN_ERR_INVALID_ARG, "workspace has %zu bytes, needs %zu", a->workspace_bytes, need);
+  return decode_impl(a, stream, false);
+}
 
-    const int64_t rows = (int64_t)a->batch * a->num_heads_q * a->num_splits;
-    char* ws = static_cast<char*>(a->workspace);
-    float* part_o = reinterpret_cast<float*>(ws);
-    const size_t lse_off = align256((size_t)rows * a->head_dim * sizeof(float));
-    float* part_lse = reinterpret_cast<float*>(ws + lse_off);
-    const size_t plan_off = lse_off + align256((size_t)rows * sizeof(float));
-    int32_t* plan = reinterpret_cast<int32_t*>(ws + plan_off);
-    int32_t* prefix = reinterpret_cast<int32_t*>(ws + plan_off + 256);
-    int32_t* start = reinterpret_cast<int32_t*>(ws + plan_off + 256 +
-                                                align256((size_t)(a->batch + 1) * sizeof(int32_t)));
-    int part = (a->max_seqlen_k + a->num_splits - 1) / a->num_splits;
-    part = ((part + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE) * ATTN_PAGE_SIZE;
-    if (part == 0) part = ATTN_PAGE_SIZE;
-
-    attn::DecodeParams p{};
-    p.q = static_cast<const uint16_t*>(a->q);
-    p.k = static_cast<const uint16_t*>(a->k_cache);
-    p.v = static_cast<const uint16_t*>(a->v_cache);
-    p.block_table = a->block_table; p.seqlens_k = a->seqlens_k;
-    p.part_o = part_o; p.part_lse = part_lse;
-    p.batch = a->batch; p.hq = a->num_heads_q; p.hkv = a->num_heads_kv; p.group = G;
-    p.num_blocks = a->num_blocks; p.max_blocks = a->max_blocks_per_seq;
-    p.max_seqlen_k = a->max_seqlen_k; p.num_splits = a->num_splits; p.part_tokens = part;
-    const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
-    p.scale_log2 = scale * 1.4426950408889634f;
-
-    p.plan = plan; p.prefix = prefix; p.start = start;
-
-    attn::CombineParams c{};
-    c.part_o = part_o; c.part_lse = part_lse; c.o = a->o; c.lse = a->lse;
-    c.pairs = a->batch * a->num_heads_q; c.num_splits = a->num_splits; c.o_dtype = a->o_dtype;
-    c.o_round = a->o_dtype == ATTN_BF16 ? a->o_round : 0;
-
-    if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    // Balanced split kernel when partitions may be cut (num_splits >= 2) and the page
-    // count per KV head fits in int32; otherwise one workgroup per fixed partition.
-    const int64_t rmax = ((int64_t)a->max_seqlen_k + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE;
-    const int cus = device_cus();
-    if (a->num_splits >= 2 && (int64_t)a->batch * rmax < (int64_t(1) << 30) && cus > 0) {
-      p.nwk = std::max(1, std::min(kMaxStreamWG, cus / a->num_heads_kv));
-      c.seqlens_k = a->seqlens_k; c.heads = a->num_heads_q; c.max_seqlen_k = a->max_seqlen_k;
-      if (attn_status_t st = launch_status(attn::launch_decode_stream(p, a->head_dim, a->qkv_dtype, s),
-                                           "decode split");
-          st != ATTN_OK)
-        return st;
-    } else if (attn_status_t st = launch_status(attn::launch_decode_split(p, a->head_dim, a->qkv_dtype, s),
-                                                "decode split");
-               st != ATTN_OK) {
-      return st;
-    }
-    return launch_status(attn::launch_combine(c, a->head_dim, s), "decode combine");
-  } catch (...) {
-    return fail(ATTN_ERR_LAUNCH, "internal error in attn_decode_fwd");
-  }
+attn_status_t attn_decode_fwd_noalloc(const attn_decode_args_t* a, void* stream) {
+  return decode_impl(a, stream, true);
 }
 
 }  // extern "C"

@@ -42,6 +42,7 @@ extern "C" {
 #define ATTN_ABI_VERSION 4
 #define ATTN_PAGE_SIZE 64      /* tokens per KV page (block_size); equal to the KV tile width */
 #define ATTN_MAX_SPLITS 64     /* upper bound of num_splits for the split-KV decode */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)  /* scratch of attn_decode_fwd_noalloc: 32 MiB */
 
 typedef enum {
   ATTN_OK = 0,
@@ -198,6 +199,25 @@ typedef struct {
 } attn_decode_args_t;
 
 attn_status_t attn_decode_fwd(const attn_decode_args_t* args, void* stream);
+
+/*
+ * Split-KV decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc. Same operation, fields
+ * and kernels as attn_decode_fwd, except that args->workspace must be NULL and
+ * args->workspace_bytes 0: the split partials and the partition plan go to a static
+ * device buffer of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends. The call allocates and frees nothing; the caller
+ * passes the inputs and the output (and lse) as for attn_decode_fwd.
+ * Every call on one device shares that device's buffer, which keeps the last call's
+ * contents (nothing in it has to start at zero: each call writes every word it reads).
+ * Calls that overlap in time on one device (on different streams, or from host threads
+ * not ordered with each other) race on the buffer and give wrong results; calls ordered
+ * on one stream are safe.
+ * Errors: as attn_decode_fwd, plus INVALID_ARG when a workspace is passed or when
+ * attn_decode_workspace_bytes(B, Hq, num_splits, d) exceeds ATTN_NOALLOC_SCRATCH_BYTES
+ * (for instance B * Hq * num_splits * d above about 8.3 million at d = 128).
+ */
+attn_status_t attn_decode_fwd_noalloc(const attn_decode_args_t* args, void* stream);
 
 /* Bytes of decode workspace: fp32 partial outputs [B, Hq, num_splits, d], then (at
  * 256-byte aligned offsets) fp32 partial lse [B, Hq, num_splits] and the partition

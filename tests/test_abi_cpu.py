@@ -37,6 +37,7 @@ def test_header_constants_match_binding():
     assert f"#define ATTN_PAGE_SIZE {_lib.ATTN_PAGE_SIZE} " in text
     assert f"#define ATTN_MAX_SPLITS {_lib.ATTN_MAX_SPLITS} " in text
     assert f"#define ATTN_ABI_VERSION {_lib.ATTN_ABI_VERSION}" in text
+    assert f"#define ATTN_NOALLOC_SCRATCH_BYTES ({_lib.ATTN_NOALLOC_SCRATCH_BYTES >> 20}u << 20)" in text
 
 
 def test_struct_sizes():
@@ -154,6 +155,22 @@ def test_combine_rejects(lib, kw, msg):
     assert msg in _lib.last_error()
 
 
+def test_decode_noalloc_rejects(lib):
+    # the allocation-free decode takes no workspace, and refuses sizes whose partials and
+    # plan would not fit its static scratch; both are host-side checks
+    st = lib.attn_decode_fwd_noalloc(ctypes.byref(decode_args()), None)
+    assert st == _lib.ATTN_ERR_INVALID_ARG and "takes no workspace" in _lib.last_error()
+    big = decode_args(workspace=None, workspace_bytes=0, batch=64, num_heads_q=64, num_heads_kv=8,
+                      num_splits=16)      # 64 * 64 * 16 * 128 * 4 bytes = 32 MiB of partials + plan
+    need = lib.attn_decode_workspace_bytes(64, 64, 16, 128)
+    assert need > _lib.ATTN_NOALLOC_SCRATCH_BYTES
+    st = lib.attn_decode_fwd_noalloc(ctypes.byref(big), None)
+    assert st == _lib.ATTN_ERR_INVALID_ARG and "maximum" in _lib.last_error()
+    st = lib.attn_decode_fwd_noalloc(ctypes.byref(decode_args(workspace=None, workspace_bytes=0, num_splits=0)),
+                                     None)
+    assert st == _lib.ATTN_ERR_INVALID_ARG and "num_splits" in _lib.last_error()
+
+
 def test_workspace_bytes(lib):
     n = lib.attn_decode_workspace_bytes(32, 32, 16, 128)
     assert n >= 32 * 32 * 16 * 129 * 4 and n % 256 == 0
@@ -167,6 +184,8 @@ def test_valid_call_without_device_reports_no_device(lib):
     assert lib.attn_decode_fwd(ctypes.byref(decode_args()), None) == _lib.ATTN_ERR_NO_DEVICE
     assert lib.attn_splitkv_combine(ctypes.byref(combine_args()), None) == _lib.ATTN_ERR_NO_DEVICE
     assert lib.attn_device_info(0, ctypes.byref(_lib.DeviceInfo())) == _lib.ATTN_ERR_NO_DEVICE
+    fits = decode_args(workspace=None, workspace_bytes=0)
+    assert lib.attn_decode_fwd_noalloc(ctypes.byref(fits), None) == _lib.ATTN_ERR_NO_DEVICE
 
 
 def test_missing_library_raises(tmp_path, monkeypatch):
