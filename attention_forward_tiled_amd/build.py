@@ -5,11 +5,22 @@
 Every HIP source is compiled for gfx950 only. Packed fp32 VALU instructions are
 disabled on purpose (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
 Objects go to ``_build/``; the shared library lands next to this file.
+
+The kernels issue their global->LDS copies (global_load_lds_dwordx4) from inline asm
+that sets m0, the LDS destination register, without the compiler knowing (the
+compiler reserves m0 and cannot take it as a clobber). That is only correct while the
+generated code keeps nothing of its own in m0. Every build therefore keeps the gfx950
+assembly (``-save-temps=obj``) and checks it: m0 may appear only as the destination of
+the ``s_mov_b32 m0, sN`` that directly precedes such a copy, and no instruction that
+reads m0 implicitly (register-indexed moves, messages, GWS) may appear. The build fails
+otherwise.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -44,10 +55,36 @@ def flags() -> list:
 EXTRA_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+# Instructions that read or write m0 implicitly on gfx9-family targets.
+_M0_IMPLICIT = re.compile(r"^\s*(s_movrel\w*|v_movrel\w*|s_set_gpr_idx_\w*|s_sendmsg\w*|ds_gws_\w*|"
+                          r"v_interp\w*|buffer_\w+\s.*\blds\b)")
+_M0 = re.compile(r"\bm0\b")
+
+
+def check_m0(asm: str) -> list:
+    """Uses of m0 in gfx950 assembly other than the LDS-copy idiom
+    ``s_mov_b32 m0, sN`` / ``s_nop 0`` / ``global_load_lds_dwordx4``; returns the offending
+    lines (empty when the invariant holds)."""
+    lines = [l.split(";", 1)[0].rstrip() for l in asm.splitlines()]
+    code = [(i, l.strip()) for i, l in enumerate(lines) if l.strip() and not l.strip().startswith((".", "//"))
+            and not l.strip().endswith(":")]
+    bad = []
+    for n, (i, l) in enumerate(code):
+        if _M0_IMPLICIT.match(l):
+            bad.append(f"line {i + 1}: {l}")
+        elif _M0.search(l):
+            ok = (re.fullmatch(r"s_mov_b32\s+m0,\s*s\d+", l) is not None and n + 2 < len(code)
+                  and code[n + 1][1] == "s_nop 0" and code[n + 2][1].startswith("global_load_lds_dwordx4"))
+            if not ok:
+                bad.append(f"line {i + 1}: {l}")
+    return bad
+
+
+def _compile(src: str, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(src, []), "-save-temps=obj", "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=build_dir)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
     if r.returncode != 0:
@@ -57,10 +94,31 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def device_asm(src: str, build_dir: str = BUILD) -> str:
+    """The gfx950 assembly that the last compile of `src` left in `build_dir`."""
+    stem = os.path.splitext(src)[0]
+    paths = glob.glob(os.path.join(build_dir, f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}*.s"))
+    if len(paths) != 1:
+        raise RuntimeError(f"expected one {ARCH} assembly file for {src} in {build_dir}, found {paths}")
+    with open(paths[0]) as f:
+        return f.read()
+
+
+def compile_all(build_dir: str = BUILD, jobs: int = 4) -> list:
+    """Compile every source into `build_dir` and check the m0 invariant of its assembly."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, build_dir), SOURCES))
+    for src in SOURCES:
+        bad = check_m0(device_asm(src, build_dir))
+        if bad:
+            raise RuntimeError(f"{src}: m0 used outside the LDS-copy idiom (the inline-asm copies would "
+                               "clobber it):\n  " + "\n  ".join(bad[:20]))
+    return objs
+
+
+def build(jobs: int = 4, verbose: bool = True) -> str:
+    objs = compile_all(BUILD, jobs)
     tmp = OUT + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -175,8 +175,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // global_load_lds_dwordx4 with a per-lane 64-bit address: lane l's 16 bytes land at LDS
 // byte lds + 16 * l. Issued from inline asm so that the compiler does not fence LDS reads
 // of the other stage on it; completion is awaited explicitly (vmcnt) before the barrier
-// that publishes the stage. The asm sets m0, which the compiler reserves (it cannot be
-// named as clobbered) and which the generated code of these kernels uses nowhere else.
+// that publishes the stage.
+// Invariant: the asm sets m0 (the copy's LDS base) behind the compiler's back, since the
+// compiler reserves m0 and cannot take it as a clobber. This is correct only while the
+// generated code itself keeps nothing in m0 (no register-indexed moves, messages or GWS
+// operations in these kernels). The build checks the gfx950 assembly of every source and
+// fails if m0 appears anywhere but in the s_mov_b32 m0 / s_nop 0 / global_load_lds_dwordx4
+// sequence below; the per-launch-form parity tests guard the copies' results.
 // NT marks the load non-temporal: for data read once (the decode's K/V pages) it keeps
 // the stream from displacing reusable lines in the caches, and the decode stream runs
 // about 12% faster with it; the prefill's K/V tiles are re-read by other workgroups
