@@ -112,6 +112,16 @@ CONFIGS = {
     "splitkv_decode_bf16_64k": DecodeCase(
         "splitkv_decode_bf16_64k", batch=32, heads_q=32, heads_kv=8, head_dim=128,
         dtype="bf16", len_lo=1024, len_hi=65536, num_splits=16),
+    # Head sizes 256 and 64 (the other two tiled paths): causal MHA self-attention over
+    # dense BSHD K/V, 4096 positions.
+    "causal_mha_bf16_d256_s4096": PrefillCase(
+        "causal_mha_bf16_d256_s4096", batch=2, heads_q=16, heads_kv=16, seqlen_q=4096,
+        seqlen_k=4096, head_dim=256, dtype="bf16", causal=True, kv="dense", layout="bshd",
+        poison=False),
+    "causal_mha_f16_d64_s4096": PrefillCase(
+        "causal_mha_f16_d64_s4096", batch=8, heads_q=32, heads_kv=32, seqlen_q=4096,
+        seqlen_k=4096, head_dim=64, dtype="f16", causal=True, kv="dense", layout="bshd",
+        poison=False),
     # Long non-causal MHA self-attention, dense BSHD K/V, inputs 0.5*N(0,1).
     "long_noncausal_bf16_s16384": PrefillCase(
         "long_noncausal_bf16_s16384", batch=4, heads_q=16, heads_kv=16, seqlen_q=16384,

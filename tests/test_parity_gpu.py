@@ -90,31 +90,39 @@ def test_named_prefill_full(name):
     assert err <= tolerance(case)
 
 
-def test_named_long_noncausal_every_workgroup():
-    # Full size, in the launch form the benchmark times (eight-wave workgroups of 256
-    # query rows, 32 rows per wave). The whole output must be written (NaN-filled before
-    # the launch, checked finite in gpu_prefill); against the oracle, every (sequence,
-    # head) gets one seeded row in every 32-row slice, so every wave of every one of the
-    # 64 x 64 workgroups is compared: 512 rows per (b, h), 32768 in all.
-    case = CONFIGS["long_noncausal_bf16_s16384"]
-    say(f"prefill parity (one row per wave of every workgroup) {case.name}")
-    inp = make_prefill_inputs(case, seed=0)
+def _every_wave_check(case, seed=0):
+    """Full-size launch; the whole output must be written (NaN-filled before the launch,
+    checked finite in gpu_prefill); against the oracle, every (sequence, head) gets one
+    seeded row in every 32-row slice of the query axis, so every wave of every workgroup
+    is compared (32 query rows per wave in every launch form). Dense BSHD inputs."""
+    inp = make_prefill_inputs(case, seed=seed)
     O, _ = gpu_prefill(inp)
-    B, S, H, d = case.batch, case.seqlen_q, case.heads_q, case.head_dim
-    rng = np.random.default_rng(0)
+    B, S, H, d, G = case.batch, case.seqlen_q, case.heads_q, case.head_dim, case.group
+    rng = np.random.default_rng(seed)
     worst, n_rows = 0.0, 0
     for b in range(B):
         for h in range(H):
-            rows = np.arange(0, S, 32) + rng.integers(0, 32, size=S // 32)
+            rows = np.arange(0, S, 32) + rng.integers(0, 32, size=-(-S // 32))
+            rows = np.minimum(rows, S - 1)
             rows[0], rows[-1] = 0, S - 1
-            K = bits_to_f64(inp.k[b, :, h, :], case.dtype)
-            V = bits_to_f64(inp.v[b, :, h, :], case.dtype)
+            K = bits_to_f64(inp.k[b, :, h // G, :], case.dtype)
+            V = bits_to_f64(inp.v[b, :, h // G, :], case.dtype)
             Oref, _ = oracle.attention_rows(bits_to_f64(inp.q[b, rows, h, :], case.dtype), K, V, rows,
-                                            case.seqlen_k, S, False, 1.0 / np.sqrt(d))
+                                            case.seqlen_k, S, case.causal, 1.0 / np.sqrt(d))
             worst = max(worst, max_abs_err(O[b, rows, h, :], Oref))
             n_rows += rows.size
     say(f"  max abs err {worst:.3e} over {n_rows} (b, h, row) triples")
     assert worst <= tolerance(case)
+
+
+@pytest.mark.parametrize("name", ["long_noncausal_bf16_s16384", "causal_mha_bf16_d256_s4096",
+                                  "causal_mha_f16_d64_s4096"])
+def test_named_full_size_every_wave(name):
+    # the long workload in the eight-wave form (4096 workgroups of 256 rows, 32768 rows
+    # checked), and the d = 256 and d = 64 causal workloads in their four-wave forms
+    case = CONFIGS[name]
+    say(f"prefill parity (one row per wave of every workgroup) {name}")
+    _every_wave_check(case)
 
 
 def test_prefill_deterministic():
