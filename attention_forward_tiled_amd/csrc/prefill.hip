@@ -471,6 +471,266 @@ void prefill_kernel(const PrefillParams p) {
   }
 }
 
+
+// Narrow form for d = 256: eight waves, two per SIMD, 16 query rows per wave, 128 per
+// workgroup. The 32-row form needs about 500 registers at d = 256 and so runs one wave per
+// SIMD, which leaves every LDS and softmax latency exposed; with 16 rows a wave holds O^T
+// in 64 registers. Products on the 16-wide atoms: S^T = K Q^T with v_mfma_f32_16x16x32
+// (K from LDS as the A operand, Q in registers), O^T += V^T P^T with the same atom over 32
+// keys (two 16-key blocks of the S^T accumulator, whose layout is the B-operand layout
+// with the keys enumerated per block), so P stays in registers; V^T comes from the
+// row-major V tile by transposed LDS reads. Waves 0-3 (one per SIMD) issue the tile copies. Lane l holds query row l % 16
+// of its wave and keys 16 kb + 4 (l / 16) + i of every 16-key block kb; the other keys of
+// the row sit in lanes l ^ 16, l ^ 32, l ^ 48. Chunks are swizzled by the 16-row pattern
+// (qswz) that keeps both read patterns free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int qswz(int row) {
+  const int r = row & 15;
+  return ((r & 7) << 1) | (r >> 3);
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(512, 1)
+void prefill_narrow_kernel(const PrefillParams p) {
+  constexpr int NW = 8;
+  constexpr int KS = D / 32;            // k-steps (32 deep) of S^T
+  constexpr int DB = D / 16;            // 16-wide d blocks of O^T
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPI = 512 / D;          // rows per 1 KiB wave-wide copy
+  constexpr int NIW = kPage / RPI / NW; // such copies per wave per tile (K and V each)
+  constexpr int TILE = kPage * D;
+  constexpr int ROWB = D * 2;
+  __shared__ __align__(16) uint16_t smem[2 * 2 * TILE];   // [2 stages][K, V][TILE]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  const int nx = gridDim.x, xcd = blockIdx.x & 7, per = nx >> 3, extra = nx & 7;
+  const int lid = xcd * per + min(xcd, extra) + (int)(blockIdx.x >> 3);
+  const int nq = (p.seqlen_q + p.bq - 1) / p.bq;
+  const int unit = lid % nq;
+  const int bh = lid / nq;
+  const int b = bh % p.batch, kvh = bh / p.batch;
+
+  int L = p.seqlen_k;
+  if (p.seqlens_k) L = min(max(scalar_load(p.seqlens_k + b), 0), p.seqlen_k);
+  int sq = p.seqlen_q;
+  int64_t qrow0 = 0;
+  if (p.cu_seqlens_q) {
+    const int c0 = scalar_load(p.cu_seqlens_q + b);
+    sq = min(max(scalar_load(p.cu_seqlens_q + b + 1) - c0, 0), p.seqlen_q);
+    qrow0 = c0;
+  }
+  const int off = L - sq;
+  const float c = p.scale_log2;
+  const int q0 = (nq - 1 - unit) * p.bq;
+
+  // this lane's query row
+  const int R = wave * 16 + lr;
+  const int hig = R / p.bq;
+  const int rpos = q0 + (R - hig * p.bq);
+  const int rh = kvh * p.group + hig;
+  const bool rok = hig < p.group && rpos < sq;
+  u32x4 qf[KS];
+  {
+    const uint16_t* qp = p.q + b * p.q_sb + (int64_t)rh * p.q_sh + (qrow0 + rpos) * p.q_ss;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = rok ? ldg16(qp + s * 32 + lg * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  const int pmax = min(q0 + p.bq, sq) - 1;
+  const int kv_end = p.causal ? min(L, pmax + off + 1) : L;
+  const int n_tiles = kv_end > 0 && q0 < sq ? (kv_end + kPage - 1) / kPage : 0;
+  int n_full = L / kPage;
+  if (p.causal) n_full = min(n_full, max(q0 + off + 1, 0) / kPage);
+  n_full = min(n_full, n_tiles);
+
+  const bool paged = p.block_table != nullptr;
+  const int64_t rs = paged ? (int64_t)p.hkv * D : p.kv_ss;
+  const int r_in = lane / CPR, pc = lane % CPR;
+  constexpr int NI2 = 2 * NIW;   // waves 0-3 copy the shares of waves (2w, 2w + 1)
+  uint32_t dma_off[NI2];
+#pragma unroll
+  for (int k = 0; k < NI2; ++k) {
+    const int row = ((wave & 3) * NI2 + k) * RPI + r_in;
+    dma_off[k] = (uint32_t)((row * rs + ((pc ^ qswz<D>(row)) << 3)) * 2);
+  }
+  const uint32_t smem_base = lds_addr(smem);
+  uint32_t stage_ok = 3u;
+  auto issue_tile = [&](int j, int stage) {
+    int64_t base;
+    bool page_ok = true;
+    if (paged) {
+      const int pg = scalar_load(p.block_table + (int64_t)b * p.max_blocks + __builtin_amdgcn_readfirstlane(j));
+      page_ok = pg >= 0 && pg < p.num_blocks;
+      base = (int64_t)(page_ok ? pg : 0) * kPage * p.hkv * D + (int64_t)kvh * D;
+    } else {
+      base = b * p.kv_sb + kvh * p.kv_sh + (int64_t)j * kPage * p.kv_ss;
+    }
+    stage_ok = page_ok ? (stage_ok | (1u << stage)) : (stage_ok & ~(1u << stage));
+    const uint32_t ks = smem_base + stage * 2 * TILE * 2;
+    const uint32_t vs = ks + TILE * 2;
+    if (wave >= 4) return;
+    if (page_ok && (j + 1) * kPage <= L) {
+#pragma unroll
+      for (int k = 0; k < NI2; ++k) {
+        const int i = wave * NI2 + k;
+        dma16_s(p.k + base, dma_off[k], ks + i * 1024);
+        dma16_s(p.v + base, dma_off[k], vs + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NI2; ++k) {
+        const int i = wave * NI2 + k;
+        const bool ok = page_ok && (j * kPage + (i * RPI + r_in) < L);
+        dma16_v(ok ? p.k + base + dma_off[k] / 2 : kZeroChunk, ks + i * 1024);
+        dma16_v(ok ? p.v + base + dma_off[k] / 2 : kZeroChunk, vs + i * 1024);
+      }
+    }
+  };
+
+  // per-lane LDS read offsets: K rows 16 kb + lr at chunk 4 s + lg (kb as an immediate);
+  // V^T reads at row 16 t + 4 lg + lr / 4 (t as an immediate), d 16 db + 4 (lr % 4)
+  uint32_t koff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) koff[s] = lr * ROWB + (((4 * s + lg) ^ qswz<D>(lr)) << 4);
+  uint32_t voff[DB];
+  {
+    const int row = 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 2 * db + ((lr & 3) >> 1);
+      voff[db] = row * ROWB + ((chunk ^ qswz<D>(row)) << 4) + 8 * (lr & 1);
+    }
+  }
+
+  float mref = -INFINITY, lsum = 0.f;
+  float4v acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int j, auto stage_c, auto mask_c) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    const char* ks = reinterpret_cast<const char*>(smem) + STAGE * 2 * TILE * 2;
+    const char* vs = ks + TILE * 2;
+    float4v sc[4];   // key block kb: keys 16 kb + 4 lg + i
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        sc[kb] = Op<T>::mfma(as_op<T>(*reinterpret_cast<const u32x4*>(ks + koff[s] + kb * 16 * ROWB)),
+                             as_op<T>(qf[s]), sc[kb]);
+    if constexpr (MASK) {
+      // key j * 64 + 16 kb + 4 lg + i is visible iff 16 kb + i < lim (one per-lane bound,
+      // compared with constants, so that no per-key value lives across the tile loop)
+      const int lim = (p.causal ? min(L, rpos + off + 1) : L) - j * kPage - 4 * lg;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[kb][i] = 16 * kb + i < lim ? sc[kb][i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[2][0], sc[2][1]), fmaxf(sc[2][2], sc[2][3])),
+                         fmaxf(fmaxf(sc[3][0], sc[3][1]), fmaxf(sc[3][2], sc[3][3]))));
+    // lazily moved reference maximum, as in prefill_kernel; the row spans lanes l, l^16,
+    // l^32, l^48
+    if (__builtin_amdgcn_ballot_w64(mx * c > mref + kLazy) != 0) {
+      const float mt = rows4_max(mx) * c;
+      const bool up = mt > mref + kLazy;
+      const float nref = up ? mt : mref;
+      const float alpha = up ? fast_exp2(mref - nref) : 1.f;
+      mref = nref;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    const float mneg = mref == -INFINITY ? 0.f : -mref;
+    u32x2 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = fast_exp2(__builtin_fmaf(sc[kb][i], c, mneg));
+      pb[kb] = u32x2{pack2<T>(y[0], y[1]), pack2<T>(y[2], y[3])};
+    }
+    float ps0 = lsum, ps1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      ps0 = Op<T>::sum2(pb[kb][0], ps0);
+      ps1 = Op<T>::sum2(pb[kb][1], ps1);
+    }
+    lsum = ps0 + ps1;
+    // O^T += V^T P^T, 32 keys per product: key blocks 2 t2 and 2 t2 + 1, enumerated in the
+    // same order in the V^T operand (two transposed reads) and in P (two packed blocks)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const u32x4 pq = u32x4{pb[2 * t2][0], pb[2 * t2][1], pb[2 * t2 + 1][0], pb[2 * t2 + 1][1]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + voff[db] + 32 * t2 * ROWB));
+        const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + voff[db] + (32 * t2 + 16) * ROWB));
+        acc[db] = Op<T>::mfma(as_op<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_op<T>(pq), acc[db]);
+      }
+    }
+  };
+
+  using Full = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  auto step = [&](int j, auto stage_c, auto mask_c) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (j + 1 < n_tiles) issue_tile(j + 1, STAGE ^ 1);
+    if ((stage_ok >> STAGE) & 1u) compute(j, stage_c, mask_c);
+  };
+  // tiles [0, n_full) need no mask, [n_full, n_tiles) do: two loops, so that each loop
+  // body holds one kind of tile (one register assignment for the loop-carried state)
+  if (n_tiles > 0) issue_tile(0, 0);
+  int j = 0;
+  for (; j + 1 < n_full; j += 2) {
+    step(j, std::integral_constant<int, 0>{}, Full{});
+    step(j + 1, std::integral_constant<int, 1>{}, Full{});
+  }
+  if (j < n_full) {
+    step(j, std::integral_constant<int, 0>{}, Full{});
+    ++j;
+  }
+  for (; j < n_tiles; ++j) {
+    if (j & 1) step(j, std::integral_constant<int, 1>{}, Masked{});
+    else step(j, std::integral_constant<int, 0>{}, Masked{});
+  }
+
+  // ---- epilogue: lane holds d = 16 db + 4 lg + i of its row
+  const float l = rows4_sum(lsum);
+  if (rok) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (qrow0 + rpos) * p.o_ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = 16 * db + 4 * lg;
+      const float4v v = acc[db] * inv;
+      if (p.o_dtype == kF32) {
+        *reinterpret_cast<float4v*>(static_cast<float*>(p.o) + ob + d0) = v;
+      } else if (p.o_dtype == kF16) {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ob + d0) =
+            u32x2{pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3])};
+      } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ob + d0) =
+            u32x2{pack_bf16_round(v[0], v[1], p.o_round), pack_bf16_round(v[2], v[3], p.o_round)};
+      }
+    }
+    if (p.lse && lg == 0) {
+      const int64_t li = p.cu_seqlens_q ? (int64_t)rh * scalar_load(p.cu_seqlens_q + p.batch) + qrow0 + rpos
+                                        : ((int64_t)b * p.hq + rh) * p.seqlen_q + rpos;
+      p.lse[li] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 // Below this many single-group workgroups (four rounds of two per CU on 256 CUs) a causal
 // launch splits the key range of each workgroup over two groups (d <= 128): the causal
 // triangle then leaves too few long workgroups to balance the CUs. (A non-causal launch
@@ -506,6 +766,11 @@ hipError_t launch_one(const PrefillParams& p0, hipStream_t stream) {
   const int64_t nq = (p.seqlen_q + p.bq - 1) / p.bq;
   const int64_t blocks = nq * p.hkv * p.batch;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if constexpr (D == 256 && !PRECISE) {
+    // d = 256: eight waves of 16 rows (two per SIMD) in place of four of 32 (one per SIMD)
+    hipLaunchKernelGGL((prefill_narrow_kernel<D, T>), dim3((unsigned)blocks), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
   if constexpr (D <= 128) {
     if (p.causal && blocks < kSplitBelow) {
       // Two-group workgroups fill a CU each. Under a causal mask, pair a heavy and a
