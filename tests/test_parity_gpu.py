@@ -41,6 +41,10 @@ SMALL = [
     P("bf16_ragged_dense", 3, 4, 4, 64, 200, 128, "bf16", False, "dense", seqlens_k=(200, 1, 130)),
     P("f16_precise_d128", 1, 2, 1, 150, 150, 128, "f16", True, "paged", out_dtype="f32", precise=True),
     P("bf16_f32_out", 1, 2, 2, 96, 96, 128, "bf16", True, "paged", out_dtype="f32"),
+    P("f16_d256_gqa3_causal_paged", 2, 6, 2, 190, 190, 256, "f16", True, "paged"),
+    P("bf16_d256_ragged_dense_bhsd", 3, 4, 4, 130, 300, 256, "bf16", True, "dense", layout="bhsd",
+      seqlens_k=(300, 64, 7)),
+    P("bf16_d256_f32_out_cross", 1, 4, 1, 333, 1000, 256, "bf16", False, "paged", out_dtype="f32"),
 ]
 
 
@@ -199,13 +203,14 @@ def test_prefill_eight_wave_sampled(case):
     assert err <= tolerance(case)
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("mode", ["rtne", "rtna", "rtz"])
-def test_prefill_bf16_output_rounding(mode):
+def test_prefill_bf16_output_rounding(mode, d):
     # the three bf16 output modes of the MoonMath benchmark page: parity against the
     # oracle rounded in the same mode, and the rounding relations against the fp32
     # output of the same launch
-    case = P("bf16_round", 2, 8, 2, 160, 300, 128, "bf16", True, "paged")
-    say(f"prefill bf16 output rounding {mode}")
+    case = P("bf16_round", 2, 8, 2, 160, 300, d, "bf16", True, "paged")
+    say(f"prefill bf16 output rounding {mode} d={d}")
     inp = make_prefill_inputs(case, seed=11)
     O, _ = gpu_prefill(inp, out_round=mode)
     O32, _ = gpu_prefill(inp, out_dtype="f32")
@@ -225,6 +230,9 @@ VARLEN = [
        seqlens_k=(130, 7, 130)), (33, 200, 1)),
     (P("bf16_d128_causal_paged_gqa4_varlen", 3, 16, 4, 700, 900, 128, "bf16", True, "paged",
        seqlens_k=(900, 700, 333)), (700, 129, 333)),
+    # d = 256 (eight waves of 16 rows): packed queries with GQA 2
+    (P("bf16_d256_causal_paged_gqa2_varlen", 3, 4, 2, 300, 700, 256, "bf16", True, "paged",
+       seqlens_k=(700, 65, 300)), (300, 1, 129)),
     # eight-wave form (max_seqlen_q 4096: 16 x 8 heads x 8 sequences = 1024 workgroups)
     (P("f16_d64_noncausal_dense_varlen_wg8", 8, 8, 8, 4096, 1000, 64, "f16", False, "dense",
        seqlens_k=(200, 64, 1, 130, 700, 5, 64, 999)), (4096, 0, 1, 255, 256, 257, 1000, 3000)),
@@ -285,6 +293,8 @@ def test_prefill_long_keys():
 BAD_ID_CASES = [
     P("bf16_d128_noncausal_paged_bad_ids", 2, 8, 2, 100, 640, 128, "bf16", False, "paged",
       seqlens_k=(640, 400)),
+    P("f16_d256_noncausal_paged_bad_ids", 2, 6, 2, 200, 640, 256, "f16", False, "paged",
+      seqlens_k=(640, 400)),
     # eight-wave form: 32 x 8 heads x 4 sequences = 1024 workgroups
     P("f16_d64_noncausal_paged_bad_ids_wg8", 4, 8, 8, 8192, 640, 64, "f16", False, "paged",
       seqlens_k=(640, 400, 640, 64)),
@@ -324,6 +334,7 @@ GROWING = [
     P("f16_d128_gqa4_causal_growing_two_groups", 1, 8, 2, 1000, 1000, 128, "f16", True, "dense"),
     P("bf16_d64_noncausal_growing_wg4", 2, 8, 2, 700, 900, 64, "bf16", False, "dense"),
     P("bf16_d128_noncausal_growing_wg8", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense"),
+    P("bf16_d256_causal_growing_narrow", 2, 6, 2, 700, 700, 256, "bf16", True, "dense"),
 ]
 
 
