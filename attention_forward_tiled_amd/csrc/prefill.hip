@@ -341,16 +341,13 @@ void prefill_kernel(const PrefillParams p) {
   // Step i of the workgroup: both groups take their i-th tile in lockstep (one barrier per
   // step publishes the stage and recycles the other); a group whose range is exhausted
   // only joins the barriers.
-  auto step = [&](int i, auto stage_c) {
+  auto step = [&](int i, auto stage_c, auto mask_c) {
     constexpr int STAGE = decltype(stage_c)::value;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     const int j = j0 + i;
     if (j + 1 < j1) issue_tile(j + 1, STAGE ^ 1);
-    if ((stage_ok >> STAGE) & 1u) {
-      if (j < n_full) compute(j, stage_c, Full{});
-      else if (j < j1) compute(j, stage_c, Masked{});
-    }
+    if (((stage_ok >> STAGE) & 1u) && j < j1) compute(j, stage_c, mask_c);
   };
 
   for (int it = 0; it < (PAIR ? 2 : 1); ++it) {
@@ -389,9 +386,22 @@ void prefill_kernel(const PrefillParams p) {
     for (int db = 0; db < DB; ++db) acc[db] = float16v{};
 
     if (j0 < j1) issue_tile(j0, 0);
-    for (int i = 0; i < h; i += 2) {
-      step(i, std::integral_constant<int, 0>{});
-      if (i + 1 < h) step(i + 1, std::integral_constant<int, 1>{});
+    // steps [0, nf) take tiles that need no mask; the rest take masked tiles or (a group
+    // whose range is exhausted) only join the barriers. Two loops, one kind of tile body
+    // each, so that each keeps one register assignment.
+    const int nf = max(0, min(n_full, j1) - j0);
+    int i = 0;
+    for (; i + 1 < nf; i += 2) {
+      step(i, std::integral_constant<int, 0>{}, Full{});
+      step(i + 1, std::integral_constant<int, 1>{}, Full{});
+    }
+    if (i < nf) {
+      step(i, std::integral_constant<int, 0>{}, Full{});
+      ++i;
+    }
+    for (; i < h; ++i) {
+      if (i & 1) step(i, std::integral_constant<int, 1>{}, Masked{});
+      else step(i, std::integral_constant<int, 0>{}, Masked{});
     }
 
     if constexpr (PAIR) {
