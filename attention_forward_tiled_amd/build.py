@@ -104,6 +104,34 @@ def device_asm(src: str, build_dir: str = BUILD) -> str:
         return f.read()
 
 
+def kernel_resources(asm: str) -> dict:
+    """Per-kernel resource figures from the code-object metadata of gfx950 assembly:
+    {mangled name: {"vgpr", "agpr", "sgpr", "vgpr_spill", "sgpr_spill", "lds", "scratch"}}."""
+    keys = {".vgpr_count": "vgpr", ".agpr_count": "agpr", ".sgpr_count": "sgpr", ".vgpr_spill_count": "vgpr_spill",
+            ".sgpr_spill_count": "sgpr_spill", ".group_segment_fixed_size": "lds",
+            ".private_segment_fixed_size": "scratch"}
+    out, cur, inside = {}, None, False
+    for line in asm.splitlines():
+        if line.startswith("amdhsa.kernels:"):
+            inside = True
+            continue
+        if not inside:
+            continue
+        if line and not line.startswith(" "):
+            break                       # the next top-level key ends the kernel list
+        if line.startswith("  - "):
+            cur = {}
+            line = "    " + line[4:]
+        if cur is None or not line.startswith("    ."):
+            continue
+        key, _, val = line.strip().partition(":")
+        if key == ".name":
+            out[val.strip()] = cur
+        elif key in keys:
+            cur[keys[key]] = int(val)
+    return out
+
+
 def compile_all(build_dir: str = BUILD, jobs: int = 4) -> list:
     """Compile every source into `build_dir` and check the m0 invariant of its assembly."""
     os.makedirs(build_dir, exist_ok=True)

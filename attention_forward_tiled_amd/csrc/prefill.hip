@@ -709,10 +709,17 @@ void prefill_narrow_kernel(const PrefillParams p) {
     step(j, std::integral_constant<int, 0>{}, Full{});
     ++j;
   }
-  for (; j < n_tiles; ++j) {
-    if (j & 1) step(j, std::integral_constant<int, 1>{}, Masked{});
-    else step(j, std::integral_constant<int, 0>{}, Masked{});
+  // the masked loop is unrolled by two as well (the stage of tile j is j % 2): a loop whose
+  // body picks one of two stage bodies at run time spills 84 registers here
+  if (j < n_tiles && (j & 1)) {
+    step(j, std::integral_constant<int, 1>{}, Masked{});
+    ++j;
   }
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, std::integral_constant<int, 0>{}, Masked{});
+    step(j + 1, std::integral_constant<int, 1>{}, Masked{});
+  }
+  if (j < n_tiles) step(j, std::integral_constant<int, 0>{}, Masked{});
 
   // ---- epilogue: lane holds d = 16 db + 4 lg + i of its row
   const float l = rows4_sum(lsum);

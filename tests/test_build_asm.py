@@ -1,5 +1,8 @@
-"""The m0 invariant of the inline-asm LDS copies, checked on freshly compiled gfx950
-assembly (CPU only: hipcc cross-compiles), and the checker itself on small samples."""
+"""The m0 invariant of the inline-asm LDS copies and the register budgets of the hot
+kernels, checked on freshly compiled gfx950 assembly (CPU only: hipcc cross-compiles),
+and the checkers themselves on small samples."""
+import re
+
 import pytest
 
 from attention_forward_tiled_amd import build
@@ -15,9 +18,58 @@ def test_checker_accepts_the_copy_idiom_and_flags_other_uses():
     assert build.check_m0("\tv_mov_b32 v0, v1 ; comment naming m0\n") == []           # comments ignored
 
 
-def test_compiled_kernels_keep_m0_for_the_copies(tmp_path):
+@pytest.fixture(scope="module")
+def built(tmp_path_factory):
     # compile_all raises if any source's gfx950 assembly uses m0 outside the idiom
-    build.compile_all(str(tmp_path), jobs=3)
-    asm = build.device_asm("prefill.hip", str(tmp_path))
+    d = str(tmp_path_factory.mktemp("asm"))
+    build.compile_all(d, jobs=3)
+    return d
+
+
+def test_compiled_kernels_keep_m0_for_the_copies(built):
+    asm = build.device_asm("prefill.hip", built)
     assert asm.count("global_load_lds_dwordx4") > 0
     assert build.check_m0(asm) == []
+
+
+def test_resource_parser_reads_the_metadata_block():
+    asm = ("\t.text\namdhsa.kernels:\n  - .agpr_count:     4\n    .args:\n      - .offset:         0\n"
+           "    .group_segment_fixed_size: 1024\n    .name:           k1\n    .private_segment_fixed_size: 8\n"
+           "    .sgpr_count:     20\n    .sgpr_spill_count: 0\n    .vgpr_count:     40\n    .vgpr_spill_count: 2\n"
+           "  - .agpr_count:     0\n    .name:           k2\n    .vgpr_count:     9\n"
+           "amdhsa.target:   amdgcn-amd-amdhsa--gfx950\n    .name:           not_a_kernel\n")
+    r = build.kernel_resources(asm)
+    assert r == {"k1": {"agpr": 4, "lds": 1024, "scratch": 8, "sgpr": 20, "sgpr_spill": 0, "vgpr": 40,
+                        "vgpr_spill": 2},
+                 "k2": {"agpr": 0, "vgpr": 9}}
+
+
+def _head_dim(name):
+    m = re.search(r"kernelILi(\d+)E", name)
+    return int(m.group(1)) if m else None
+
+
+def test_hot_kernels_fit_their_register_budgets(built):
+    """Two waves per SIMD (eight-wave workgroups, or two four-wave workgroups per CU) need
+    at most 256 registers (VGPR + AGPR) a lane; spills to scratch memory are confined to
+    the precise d = 256 path and the paired two-group form (2 registers, outside the
+    tile loop); every kernel fits the 160 KiB of LDS of a CU."""
+    pre = build.kernel_resources(build.device_asm("prefill.hip", built))
+    dec = build.kernel_resources(build.device_asm("decode.hip", built))
+    narrow = [k for k in pre if "prefill_narrow_kernel" in k]
+    main = [k for k in pre if "14prefill_kernel" in k]
+    assert len(narrow) == 2 and len(main) == 36
+    for k in narrow:
+        r = pre[k]
+        assert r["vgpr_spill"] == 0 and r["scratch"] == 0, (k, r)
+        assert r["vgpr"] + r["agpr"] <= 256, (k, r)
+    for k in main:
+        r, d = pre[k], _head_dim(k)
+        if d == 256:
+            continue                     # precise d = 256: one wave per SIMD, 512 registers
+        assert r["vgpr"] + r["agpr"] <= 256, (k, r)
+        assert r["vgpr_spill"] <= (2 if d == 128 else 0), (k, r)
+    for k, r in dec.items():
+        assert r["vgpr_spill"] == 0 and r["scratch"] == 0, (k, r)
+    for k, r in {**pre, **dec}.items():
+        assert r["lds"] <= 160 * 1024, (k, r)
