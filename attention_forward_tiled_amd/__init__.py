@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     attn_decode_workspace_bytes,
     attn_device_info,
     attn_prefill_fwd,
+    attn_prefill_workspace_bytes,
     attn_splitkv_combine,
 )
 from ._lib import load as load_library  # noqa: F401

@@ -19,11 +19,11 @@ ATTN_ROUND_RTNE, ATTN_ROUND_RTNA, ATTN_ROUND_RTZ = 0, 1, 2
 ATTN_PAGE_SIZE = 64
 ATTN_MAX_SPLITS = 64
 ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
-ATTN_ABI_VERSION = 4
+ATTN_ABI_VERSION = 5
 
 EXPORTS = ("attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes",
            "attn_splitkv_combine", "attn_last_error", "attn_abi_version", "attn_device_count",
-           "attn_device_info", "attn_decode_fwd_noalloc")
+           "attn_device_info", "attn_decode_fwd_noalloc", "attn_prefill_workspace_bytes")
 
 _c_void_p, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -36,7 +36,8 @@ class PrefillArgs(ctypes.Structure):
                 ("seqlen_q", _i32), ("seqlen_k", _i32), ("head_dim", _i32),
                 ("num_blocks", _i32), ("max_blocks_per_seq", _i32),
                 ("qkv_dtype", _i32), ("o_dtype", _i32), ("layout", _i32),
-                ("causal", _i32), ("precise", _i32), ("scale", _f32), ("o_round", _i32)]
+                ("causal", _i32), ("precise", _i32), ("scale", _f32), ("o_round", _i32),
+                ("kv_splits", _i32), ("workspace", _c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -77,6 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.attn_prefill_fwd.argtypes = [ctypes.POINTER(PrefillArgs), _c_void_p]
     lib.attn_prefill_fwd.restype = ctypes.c_int
+    lib.attn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
+    lib.attn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_fwd.argtypes = [ctypes.POINTER(DecodeArgs), _c_void_p]
     lib.attn_decode_fwd.restype = ctypes.c_int
     lib.attn_decode_fwd_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _c_void_p]

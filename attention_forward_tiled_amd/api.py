@@ -61,6 +61,7 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
                      out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
                      scale: float = 0.0, precise: bool = False, out_round: str = "rtne",
                      cu_seqlens_q: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+                     kv_splits: int = 0, workspace: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
     """Tiled attention forward. q: [B,S_q,Hq,d] (bshd) or [B,Hq,S_q,d] (bhsd).
 
@@ -71,6 +72,12 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     Packed queries: with ``cu_seqlens_q`` ([B+1] int32, first row of each sequence)
     q and the output are [total_q, Hq, d] and ``max_seqlen_q`` bounds the per-sequence
     query counts; lse, when given, is [Hq, total_q].
+
+    Tail split (non-causal, d <= 128): ``kv_splits`` 0 lets the library split the key
+    range of the last round of work items when that round would leave half of the CUs
+    idle, 1 turns it off, n >= 2 splits those items into n parts. The partials go to ``workspace``
+    (uint8 device tensor of at least attn_prefill_workspace_bytes bytes), allocated here
+    when the call needs one and none is given.
     """
     _need(q, "q", (torch.float16, torch.bfloat16))
     _need(k, "k", (q.dtype,))
@@ -123,9 +130,37 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     a = _lib.PrefillArgs(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(block_table), _ptr(seqlens_k),
         _ptr(cu_seqlens_q), B, Hq, Hkv, Sq, Sk, d, num_blocks, max_blocks, _DT[q.dtype], _DT[out.dtype],
-        _LAYOUT[layout], int(bool(causal)), int(bool(precise)), float(scale), _round(out_round))
-    _check(_lib.load().attn_prefill_fwd(ctypes.byref(a), _stream(stream)))
+        _LAYOUT[layout], int(bool(causal)), int(bool(precise)), float(scale), _round(out_round),
+        int(kv_splits), None, 0)
+    lib = _lib.load()
+    if workspace is None and int(kv_splits) != 1:
+        need = int(lib.attn_prefill_workspace_bytes(ctypes.byref(a)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,))
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(lib.attn_prefill_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def attn_prefill_workspace_bytes(q: torch.Tensor, *, num_heads_kv: int, seqlen_k: int, causal: bool,
+                                 layout: str = "bshd", precise: bool = False, kv_splits: int = 0,
+                                 cu_seqlens_q: Optional[torch.Tensor] = None,
+                                 max_seqlen_q: Optional[int] = None) -> int:
+    """Workspace bytes attn_prefill_fwd uses for its tail split with these shapes on the
+    current device (0: the call does not split)."""
+    if cu_seqlens_q is not None:
+        B, (_, Hq, d), Sq = cu_seqlens_q.numel() - 1, q.shape, int(max_seqlen_q)
+    elif layout == "bshd":
+        B, Sq, Hq, d = q.shape
+    else:
+        B, Hq, Sq, d = q.shape
+    a = _lib.PrefillArgs(
+        None, None, None, None, None, None, None, _ptr(cu_seqlens_q), B, Hq, int(num_heads_kv), Sq, int(seqlen_k),
+        d, 0, 0, _DT[q.dtype], _DT[q.dtype], _LAYOUT[layout], int(bool(causal)), int(bool(precise)), 0.0, 0,
+        int(kv_splits), None, 0)
+    return int(_lib.load().attn_prefill_workspace_bytes(ctypes.byref(a)))
 
 
 def attn_decode_workspace_bytes(batch: int, num_heads_q: int, num_splits: int, head_dim: int) -> int:

@@ -289,88 +289,149 @@ attn_status_t attn_device_info(int32_t device, attn_device_info_t* info) {
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a prefill call's sizes, enums and alignments (pointers are not
+// required to be set) and its kernel parameters.
+attn_status_t prefill_setup(const attn_prefill_args_t* a, attn::PrefillParams* p) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->batch < 0 || a->seqlen_q < 0) return fail(ATTN_ERR_INVALID_ARG, "batch and seqlen_q must be >= 0");
+  if (a->qkv_dtype != ATTN_F16 && a->qkv_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
+  if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
+    return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+  if (attn_status_t st = check_round(a->o_round, a->o_dtype); st != ATTN_OK) return st;
+  if (a->layout != ATTN_BSHD && a->layout != ATTN_BHSD)
+    return fail(ATTN_ERR_INVALID_ARG, "layout must be ATTN_BSHD or ATTN_BHSD");
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (a->precise != 0 && a->precise != 1) return fail(ATTN_ERR_INVALID_ARG, "precise must be 0 or 1");
+  if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
+  if (a->num_heads_q <= 0 || a->num_heads_kv <= 0)
+    return fail(ATTN_ERR_INVALID_ARG, "head counts must be positive");
+  if (a->num_heads_q % a->num_heads_kv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
+                a->num_heads_q, a->num_heads_kv);
+  const int G = a->num_heads_q / a->num_heads_kv;
+  if (G > 128) return fail(ATTN_ERR_UNSUPPORTED, "GQA ratio %d above 128 is not supported", G);
+  if (a->seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "seqlen_k must be >= 0");
+  if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (a->batch > kMaxGridYZ || a->num_heads_kv > kMaxGridYZ)
+    return fail(ATTN_ERR_UNSUPPORTED, "batch and num_heads_kv must be <= %lld", (long long)kMaxGridYZ);
+  const bool paged = a->block_table != nullptr;
+  if (paged) {
+    if (!a->seqlens_k) return fail(ATTN_ERR_INVALID_ARG, "paged K/V requires seqlens_k");
+    if (a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
+      return fail(ATTN_ERR_INVALID_ARG, "paged K/V requires num_blocks > 0 and max_blocks_per_seq > 0");
+    if ((int64_t)a->max_blocks_per_seq * ATTN_PAGE_SIZE < a->seqlen_k)
+      return fail(ATTN_ERR_INVALID_ARG, "block table holds %lld keys, fewer than seqlen_k = %d",
+                  (long long)a->max_blocks_per_seq * ATTN_PAGE_SIZE, a->seqlen_k);
+    if (!aligned4(a->block_table)) return fail(ATTN_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+  }
+  if (a->seqlens_k && !aligned4(a->seqlens_k)) return fail(ATTN_ERR_INVALID_ARG, "seqlens_k must be 4-byte aligned");
+  if (a->cu_seqlens_q) {
+    if (a->layout != ATTN_BSHD) return fail(ATTN_ERR_INVALID_ARG, "packed queries (cu_seqlens_q) need the BSHD layout");
+    if (!aligned4(a->cu_seqlens_q)) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q must be 4-byte aligned");
+  }
+  if (a->kv_splits < 0 || a->kv_splits > ATTN_MAX_SPLITS)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_splits must be in [0, %d] (got %d)", ATTN_MAX_SPLITS, a->kv_splits);
+  const int64_t D = a->head_dim, Sq = a->seqlen_q, Sk = a->seqlen_k;
+  const int64_t Hq = a->num_heads_q, Hkv = a->num_heads_kv;
+  p->q = static_cast<const uint16_t*>(a->q);
+  p->k = static_cast<const uint16_t*>(a->k);
+  p->v = static_cast<const uint16_t*>(a->v);
+  p->o = a->o;
+  p->lse = a->lse;
+  p->block_table = a->block_table;
+  p->seqlens_k = a->seqlens_k;
+  if (a->layout == ATTN_BSHD) {
+    p->q_sb = Sq * Hq * D; p->q_sh = D; p->q_ss = Hq * D;
+    p->kv_sb = Sk * Hkv * D; p->kv_sh = D; p->kv_ss = Hkv * D;
+  } else {
+    p->q_sb = Hq * Sq * D; p->q_sh = Sq * D; p->q_ss = D;
+    p->kv_sb = Hkv * Sk * D; p->kv_sh = Sk * D; p->kv_ss = D;
+  }
+  if (a->cu_seqlens_q) p->q_sb = 0;   // packed: rows of every sequence in one [total_q, Hq, d]
+  p->o_sb = p->q_sb; p->o_sh = p->q_sh; p->o_ss = p->q_ss;
+  p->cu_seqlens_q = a->cu_seqlens_q;
+  p->batch = a->batch; p->hq = a->num_heads_q; p->hkv = a->num_heads_kv; p->group = G;
+  p->seqlen_q = a->seqlen_q; p->seqlen_k = a->seqlen_k;
+  p->num_blocks = a->num_blocks; p->max_blocks = a->max_blocks_per_seq;
+  p->bq = 128 / G;
+  p->causal = a->causal; p->o_dtype = a->o_dtype;
+  p->o_round = a->o_dtype == ATTN_BF16 ? a->o_round : 0;
+  const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+  p->scale_log2 = scale * 1.4426950408889634f;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 attn_status_t attn_prefill_fwd(const attn_prefill_args_t* a, void* stream) {
   try {
-    if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
-    if (a->batch < 0 || a->seqlen_q < 0) return fail(ATTN_ERR_INVALID_ARG, "batch and seqlen_q must be >= 0");
-    if (a->qkv_dtype != ATTN_F16 && a->qkv_dtype != ATTN_BF16)
-      return fail(ATTN_ERR_INVALID_ARG, "qkv_dtype must be ATTN_F16 or ATTN_BF16");
-    if (a->o_dtype != ATTN_F16 && a->o_dtype != ATTN_BF16 && a->o_dtype != ATTN_F32)
-      return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
-    if (attn_status_t st = check_round(a->o_round, a->o_dtype); st != ATTN_OK) return st;
-    if (a->layout != ATTN_BSHD && a->layout != ATTN_BHSD)
-      return fail(ATTN_ERR_INVALID_ARG, "layout must be ATTN_BSHD or ATTN_BHSD");
-    if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (a->precise != 0 && a->precise != 1) return fail(ATTN_ERR_INVALID_ARG, "precise must be 0 or 1");
-    if (!valid_d(a->head_dim)) return fail(ATTN_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
-    if (a->num_heads_q <= 0 || a->num_heads_kv <= 0)
-      return fail(ATTN_ERR_INVALID_ARG, "head counts must be positive");
-    if (a->num_heads_q % a->num_heads_kv != 0)
-      return fail(ATTN_ERR_INVALID_ARG, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
-                  a->num_heads_q, a->num_heads_kv);
-    const int G = a->num_heads_q / a->num_heads_kv;
-    if (G > 128) return fail(ATTN_ERR_UNSUPPORTED, "GQA ratio %d above 128 is not supported", G);
-    if (a->seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "seqlen_k must be >= 0");
-    if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
-    if (a->batch > kMaxGridYZ || a->num_heads_kv > kMaxGridYZ)
-      return fail(ATTN_ERR_UNSUPPORTED, "batch and num_heads_kv must be <= %lld", (long long)kMaxGridYZ);
-    const bool paged = a->block_table != nullptr;
-    if (paged) {
-      if (!a->seqlens_k) return fail(ATTN_ERR_INVALID_ARG, "paged K/V requires seqlens_k");
-      if (a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
-        return fail(ATTN_ERR_INVALID_ARG, "paged K/V requires num_blocks > 0 and max_blocks_per_seq > 0");
-      if ((int64_t)a->max_blocks_per_seq * ATTN_PAGE_SIZE < a->seqlen_k)
-        return fail(ATTN_ERR_INVALID_ARG, "block table holds %lld keys, fewer than seqlen_k = %d",
-                    (long long)a->max_blocks_per_seq * ATTN_PAGE_SIZE, a->seqlen_k);
-      if (!aligned4(a->block_table)) return fail(ATTN_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
-    }
-    if (a->seqlens_k && !aligned4(a->seqlens_k)) return fail(ATTN_ERR_INVALID_ARG, "seqlens_k must be 4-byte aligned");
-    if (a->cu_seqlens_q) {
-      if (a->layout != ATTN_BSHD) return fail(ATTN_ERR_INVALID_ARG, "packed queries (cu_seqlens_q) need the BSHD layout");
-      if (!aligned4(a->cu_seqlens_q)) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q must be 4-byte aligned");
-    }
+    attn::PrefillParams p{};
+    if (attn_status_t st = prefill_setup(a, &p); st != ATTN_OK) return st;
+    if (a->workspace && (reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (!a->workspace && a->workspace_bytes != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "workspace_bytes must be 0 without a workspace");
+    if (a->kv_splits >= 2 && !a->workspace)
+      return fail(ATTN_ERR_INVALID_ARG, "kv_splits = %d needs a workspace (attn_prefill_workspace_bytes)", a->kv_splits);
     if (a->batch == 0 || a->seqlen_q == 0) return ok();
     if (!a->q || !a->k || !a->v || !a->o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
       return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
     if (a->lse && !aligned4(a->lse)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
 
-    const int64_t D = a->head_dim, Sq = a->seqlen_q, Sk = a->seqlen_k;
-    const int64_t Hq = a->num_heads_q, Hkv = a->num_heads_kv;
-    attn::PrefillParams p{};
-    p.q = static_cast<const uint16_t*>(a->q);
-    p.k = static_cast<const uint16_t*>(a->k);
-    p.v = static_cast<const uint16_t*>(a->v);
-    p.o = a->o;
-    p.lse = a->lse;
-    p.block_table = a->block_table;
-    p.seqlens_k = a->seqlens_k;
-    if (a->layout == ATTN_BSHD) {
-      p.q_sb = Sq * Hq * D; p.q_sh = D; p.q_ss = Hq * D;
-      p.kv_sb = Sk * Hkv * D; p.kv_sh = D; p.kv_ss = Hkv * D;
-    } else {
-      p.q_sb = Hq * Sq * D; p.q_sh = Sq * D; p.q_ss = D;
-      p.kv_sb = Hkv * Sk * D; p.kv_sh = Sk * D; p.kv_ss = D;
-    }
-    if (a->cu_seqlens_q) p.q_sb = 0;   // packed: rows of every sequence in one [total_q, Hq, d]
-    p.o_sb = p.q_sb; p.o_sh = p.q_sh; p.o_ss = p.q_ss;
-    p.cu_seqlens_q = a->cu_seqlens_q;
-    p.batch = a->batch; p.hq = a->num_heads_q; p.hkv = a->num_heads_kv; p.group = G;
-    p.seqlen_q = a->seqlen_q; p.seqlen_k = a->seqlen_k;
-    p.num_blocks = a->num_blocks; p.max_blocks = a->max_blocks_per_seq;
-    p.bq = 128 / G;
-    p.cus = device_cus();
-    p.causal = a->causal; p.o_dtype = a->o_dtype;
-    p.o_round = a->o_dtype == ATTN_BF16 ? a->o_round : 0;
-    const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
-    p.scale_log2 = scale * 1.4426950408889634f;
-
     if (attn_status_t st = device_ready(); st != ATTN_OK) return st;
-    return launch_status(attn::launch_prefill(p, a->head_dim, a->qkv_dtype, a->precise != 0,
+    p.cus = device_cus();
+    attn::PrefillPlan plan{};
+    if (hipError_t e = attn::plan_prefill(p, a->head_dim, a->qkv_dtype, a->precise != 0,
+                                          a->workspace ? a->kv_splits : 1, &plan);
+        e != hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "prefill plan failed: %s", hipGetErrorString(e));
+    if (plan.parts >= 2) {
+      if (a->workspace_bytes < plan.bytes)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes, the tail split needs %zu",
+                    a->workspace_bytes, plan.bytes);
+      char* ws = static_cast<char*>(a->workspace);
+      p.part_o = reinterpret_cast<float*>(ws + plan.part_o_off);
+      p.part_lse = reinterpret_cast<float*>(ws + plan.part_lse_off);
+      p.row_off = reinterpret_cast<int64_t*>(ws + plan.row_off_off);
+      p.row_lse = reinterpret_cast<int64_t*>(ws + plan.row_lse_off);
+    }
+    return launch_status(attn::launch_prefill(p, plan, a->head_dim, a->qkv_dtype, a->precise != 0,
                                               static_cast<hipStream_t>(stream)),
                          "prefill");
   } catch (...) {
     return fail(ATTN_ERR_LAUNCH, "internal error in attn_prefill_fwd");
+  }
+}
+
+size_t attn_prefill_workspace_bytes(const attn_prefill_args_t* a) {
+  // a size query: the checks below leave the thread's last error message as it was
+  const std::string saved = g_last_error;
+  struct Restore {
+    const std::string& s;
+    ~Restore() { g_last_error = s; }
+  } restore{saved};
+  try {
+    attn::PrefillParams p{};
+    if (prefill_setup(a, &p) != ATTN_OK) return 0;
+    if (a->batch == 0 || a->seqlen_q == 0 || a->kv_splits == 1) return 0;
+    if (device_ready() != ATTN_OK) return 0;
+    p.cus = device_cus();
+    attn::PrefillPlan plan{};
+    if (attn::plan_prefill(p, a->head_dim, a->qkv_dtype, a->precise != 0, a->kv_splits, &plan) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    return plan.parts >= 2 ? plan.bytes : 0;
+  } catch (...) {
+    return 0;
   }
 }
 

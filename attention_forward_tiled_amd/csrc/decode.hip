@@ -691,7 +691,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
   }
 }
 
-// One wave per (sequence, head): lane s holds split s's lse.
+// One wave per (sequence, head), or per query row of a prefill tail split (row map):
+// lane s holds split s's lse.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p) {
   constexpr int PER = D / 64;
@@ -699,15 +700,21 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
   const int pair = blockIdx.x * kWaves + wave;
   if (pair >= p.pairs) return;
   const int S = p.num_splits;
+  int64_t obase = (int64_t)pair * D, li = pair;
+  if (p.row_off) {
+    obase = p.row_off[pair];
+    if (obase < 0) return;                          // padding row of a work item
+    li = p.row_lse[pair];
+  }
   if (p.seqlens_k && min(scalar_load(p.seqlens_k + pair / p.heads), p.max_seqlen_k) <= 0) {
     // a sequence with no key: no partial was written for it
-    const int64_t ob = (int64_t)pair * D + lane * PER;
+    const int64_t ob = obase + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       if (p.o_dtype == kF32) static_cast<float*>(p.o)[ob + e] = 0.f;
       else static_cast<uint16_t*>(p.o)[ob + e] = 0;
     }
-    if (p.lse && lane == 0) p.lse[pair] = -INFINITY;
+    if (p.lse && lane == 0 && li >= 0) p.lse[li] = -INFINITY;
     return;
   }
   const float l = lane < S ? p.part_lse[(int64_t)pair * S + lane] : -INFINITY;
@@ -730,7 +737,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
     for (int e = 0; e < PER; ++e) o[e] = fmaf(ws, src[e], o[e]);
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int64_t ob = (int64_t)pair * D + lane * PER;
+  const int64_t ob = obase + lane * PER;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const float v = o[e] * inv;
@@ -739,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
     else static_cast<uint16_t*>(p.o)[ob + e] =
         p.o_round == 0 ? Op<BF16>::from_float(v) : (uint16_t)bf16_bits_directed(v, p.o_round);
   }
-  if (p.lse && lane == 0) p.lse[pair] = den > 0.f ? M + __logf(den) : -INFINITY;
+  if (p.lse && lane == 0 && li >= 0) p.lse[li] = den > 0.f ? M + __logf(den) : -INFINITY;
 }
 
 template <int D, typename T>

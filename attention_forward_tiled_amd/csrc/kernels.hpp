@@ -27,6 +27,25 @@ struct PrefillParams {
   int32_t o_round;              // rounding of a bf16 output: 0 RTNE, 1 RTNA, 2 RTZ
   float scale_log2;             // softmax scale * log2(e)
   int32_t cus;                  // compute units of the device (work pairing decision)
+  // Tail split (non-causal launches whose last round of work items would leave CUs idle):
+  // a second launch gives each of the last items' key tiles to split_parts workgroups,
+  // which write fp32 partials that the combine merges. split_parts = 0 in ordinary
+  // launches. In a split launch, workgroup unit u takes part u % split_parts of item
+  // split_item0 + u / split_parts.
+  int32_t split_parts, split_item0;
+  float* part_o;                // [tail rows, split_parts, d]: O of each part, normalised
+  float* part_lse;              // [tail rows, split_parts]: natural-log lse of each part
+  int64_t* row_off;             // [tail rows]: element offset of the row in o, -1 if no row
+  int64_t* row_lse;             // [tail rows]: index of the row in lse, -1 if none
+};
+
+// What a prefill launch does with a given shape on the current device (host side).
+struct PrefillPlan {
+  int64_t items;                // work items of the chosen launch form
+  int32_t rows;                 // query rows per item (32 per wave)
+  int32_t parts;                // key parts per tail item (0: no tail split)
+  int64_t tail;                 // items split (the last `tail` items)
+  size_t part_o_off, part_lse_off, row_off_off, row_lse_off, bytes;   // workspace layout
 };
 
 struct DecodeParams {
@@ -58,11 +77,22 @@ struct CombineParams {
   int32_t max_seqlen_k;
   int32_t pairs, num_splits, o_dtype;
   int32_t o_round;              // rounding of a bf16 output: 0 RTNE, 1 RTNA, 2 RTZ
+  // optional row map (prefill tail splits): pair i goes to element offset row_off[i] of o
+  // (skipped when negative) and to lse[row_lse[i]] (none when negative)
+  const int64_t* row_off;
+  const int64_t* row_lse;
 };
 
+// Launch form and tail split of a prefill launch (kv_splits: 0 = chosen by the library,
+// 1 = never split, n >= 2 = split the tail items into n parts). Returns hipSuccess or the
+// error of the occupancy query.
+hipError_t plan_prefill(const PrefillParams& p, int head_dim, int qkv_dtype, bool precise, int kv_splits,
+                        PrefillPlan* plan);
 // Each launcher returns hipSuccess or the launch error; shapes were validated by the caller.
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, int qkv_dtype, bool precise,
-                          hipStream_t stream);
+// With plan.parts >= 2, p.part_o, p.part_lse, p.row_off and p.row_lse point into a
+// workspace laid out as the plan says.
+hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, int head_dim, int qkv_dtype,
+                          bool precise, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, int qkv_dtype,
                                hipStream_t stream);
 // Plan kernel then the balanced split kernel (num_splits >= 2); grid = nwk * hkv.

@@ -104,12 +104,18 @@ void prefill_kernel(const PrefillParams p) {
   const int nx = gridDim.x, xcd = blockIdx.x & 7, per = nx >> 3, extra = nx & 7;
   const int lid = xcd * per + min(xcd, extra) + (int)(blockIdx.x >> 3);
   const int nq = (p.seqlen_q + p.bq - 1) / p.bq;
+  // In a tail-split launch, `lid` numbers (item, key part) units, the parts of an item
+  // next to each other.
+  constexpr bool CAN_SPLIT = NG == 1 && !PAIR && !PRECISE;   // the forms a tail split uses
+  const int nsp = CAN_SPLIT ? p.split_parts : 0;
+  const int item = nsp ? p.split_item0 + lid / nsp : lid;
+  const int part = nsp ? lid % nsp : 0;
   // With pairing, a workgroup takes query blocks nq - 1 - u and u of one (sequence, KV
   // head) one after the other; under a causal mask their tile counts add up to about the
   // same total for every u.
   const int nu = PAIR ? (nq + 1) / 2 : nq;
-  const int unit = lid % nu;
-  const int bh = lid / nu;
+  const int unit = item % nu;
+  const int bh = item / nu;
   const int b = bh % p.batch, kvh = bh / p.batch;
 
   int L = p.seqlen_k;
@@ -378,6 +384,13 @@ void prefill_kernel(const PrefillParams p) {
       h = (n_tiles + NG - 1) / NG;
       j0 = grp * h;
       j1 = min(n_tiles, j0 + h);
+      if (nsp) {
+        // tail split (one group): this unit's share of the key tiles
+        const int tp = (n_tiles + nsp - 1) / nsp;
+        j0 = min(part * tp, n_tiles);
+        j1 = min(n_tiles, j0 + tp);
+        h = j1 - j0;
+      }
     }
 
     mref = -INFINITY;
@@ -450,9 +463,35 @@ void prefill_kernel(const PrefillParams p) {
 
     // ---- epilogue: O = o / l, lse = ln 2 * (mref + log2 l); lane holds d = 32*db + 8*g + 4*half + i
     const float l = wave_sum_xor(lsum, 32);
-    if (grp == 0 && rok) {
+    // element offset of the row in o; its index in lse: [B, Hq, S_q], or [Hq, total_q] for
+    // packed queries
+    auto o_offset = [&]() { return b * p.o_sb + (int64_t)rh * p.o_sh + (qrow0 + rpos) * p.o_ss; };
+    auto lse_index = [&]() {
+      return p.cu_seqlens_q ? (int64_t)rh * scalar_load(p.cu_seqlens_q + p.batch) + qrow0 + rpos
+                            : ((int64_t)b * p.hq + rh) * p.seqlen_q + rpos;
+    };
+    if (CAN_SPLIT && nsp) {
+      // tail split: this part's normalised O and lse in fp32, for the combine; part 0 also
+      // records where the row goes (-1 for a padding row)
+      const int64_t prow = (int64_t)(lid / nsp) * (32 * NW) + wave * 32 + lq;
+      if (rok) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float* po = p.part_o + (prow * nsp + part) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4v*>(po + 32 * db + 8 * g + 4 * half) =
+                float4v{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]} * inv;
+        if (half == 0) p.part_lse[prow * nsp + part] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+      }
+      if (half == 0 && part == 0) {
+        p.row_off[prow] = rok ? o_offset() : -1;
+        p.row_lse[prow] = rok && p.lse ? lse_index() : -1;
+      }
+    } else if (grp == 0 && rok) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (qrow0 + rpos) * p.o_ss;
+    const int64_t ob = o_offset();
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -470,12 +509,7 @@ void prefill_kernel(const PrefillParams p) {
         }
       }
     }
-    if (p.lse && half == 0) {
-      // [B, Hq, S_q], or [Hq, total_q] for packed queries
-      const int64_t li = p.cu_seqlens_q ? (int64_t)rh * scalar_load(p.cu_seqlens_q + p.batch) + qrow0 + rpos
-                                        : ((int64_t)b * p.hq + rh) * p.seqlen_q + rpos;
-      p.lse[li] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
-    }
+    if (p.lse && half == 0) p.lse[lse_index()] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
     }
     if constexpr (PAIR) __syncthreads();   // the LDS of this item is the next item's staging area
   }
@@ -757,14 +791,24 @@ constexpr int64_t kSplitBelow = 2048;
 
 template <int D, int NG, int NW, typename T, bool PRECISE, bool PAIR = false>
 hipError_t launch_ng(const PrefillParams& p, int64_t blocks, hipStream_t stream) {
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((prefill_kernel<D, NG, NW, T, PRECISE, PAIR>), dim3((unsigned)blocks),
                      dim3(64 * NW * NG), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, typename T, bool PRECISE>
-hipError_t launch_one(const PrefillParams& p0, hipStream_t stream) {
-  PrefillParams p = p0;
+// Launch form of a prefill: which kernel, its query positions per item and its item count.
+struct Form {
+  int nw = 4, ng = 1;
+  bool pair = false, narrow = false;
+  int bq = 0;
+  int64_t blocks = 0;     // workgroups of the launch
+  int64_t items = 0;      // work items (query blocks of one (sequence, KV head))
+};
+
+template <int D, bool PRECISE>
+Form choose_form(const PrefillParams& p) {
+  Form f;
   if constexpr (D <= 128) {
     // Large launches: eight-wave workgroups of 256 query rows share each K/V tile, as long
     // as that still leaves at least four workgroups per CU.
@@ -772,50 +816,178 @@ hipError_t launch_one(const PrefillParams& p0, hipStream_t stream) {
     // spans 256 positions, four of its tiles straddle the diagonal, and at these lengths
     // that costs more than the shared copies save (8% at 4096, even at 8192).
     const bool diag_heavy = p.causal && p.group == 1 && p.seqlen_k < 8192;
-    p.bq = 256 / p.group;
-    const int64_t blocks8 = (int64_t)((p.seqlen_q + p.bq - 1) / p.bq) * p.hkv * p.batch;
+    const int bq8 = 256 / p.group;
+    const int64_t blocks8 = (int64_t)((p.seqlen_q + bq8 - 1) / bq8) * p.hkv * p.batch;
     if (!diag_heavy && blocks8 >= 4 * (int64_t)std::max(p.cus, 1)) {
-      if (blocks8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-      return launch_ng<D, 1, 8, T, PRECISE>(p, blocks8, stream);
+      f.nw = 8; f.bq = bq8; f.blocks = f.items = blocks8;
+      return f;
     }
   }
-  p.bq = 128 / p.group;
-  const int64_t nq = (p.seqlen_q + p.bq - 1) / p.bq;
-  const int64_t blocks = nq * p.hkv * p.batch;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  f.bq = 128 / p.group;
+  const int64_t nq = (p.seqlen_q + f.bq - 1) / f.bq;
+  f.blocks = f.items = nq * p.hkv * p.batch;
   if constexpr (D == 256 && !PRECISE) {
     // d = 256: eight waves of 16 rows (two per SIMD) in place of four of 32 (one per SIMD)
-    hipLaunchKernelGGL((prefill_narrow_kernel<D, T>), dim3((unsigned)blocks), dim3(512), 0, stream, p);
-    return hipGetLastError();
+    f.narrow = true; f.nw = 8;
+    return f;
   }
   if constexpr (D <= 128) {
-    if (p.causal && blocks < kSplitBelow) {
+    if (p.causal && f.blocks < kSplitBelow) {
       // Two-group workgroups fill a CU each. Under a causal mask, pair a heavy and a
       // light query block per workgroup when that still leaves a workgroup per CU.
-      if (nq > 1 && blocks >= 2 * (int64_t)std::max(p.cus, 1)) {
-        return launch_ng<D, 2, 4, T, PRECISE, true>(p, (nq + 1) / 2 * p.hkv * p.batch, stream);
+      f.ng = 2;
+      if (nq > 1 && f.blocks >= 2 * (int64_t)std::max(p.cus, 1)) {
+        f.pair = true;
+        f.blocks = (nq + 1) / 2 * p.hkv * p.batch;
       }
-      return launch_ng<D, 2, 4, T, PRECISE>(p, blocks, stream);
     }
   }
-  return launch_ng<D, 1, 4, T, PRECISE>(p, blocks, stream);
+  return f;
+}
+
+// Workgroups of one-group form NW that stay resident on a CU at once (registers and LDS
+// of the compiled kernel), asked once per kernel.
+template <int D, int NW, typename T, bool PRECISE>
+hipError_t resident_per_cu(int* n) {
+  static int cached = 0;
+  if (cached > 0) {
+    *n = cached;
+    return hipSuccess;
+  }
+  int v = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &v, reinterpret_cast<const void*>(&prefill_kernel<D, 1, NW, T, PRECISE, false>), 64 * NW, 0);
+  if (e != hipSuccess) return e;
+  cached = std::max(v, 1);
+  *n = cached;
+  return hipSuccess;
+}
+
+// Tail split: only for launches whose items all have the same key range (non-causal, one
+// group); the split pays once the items are long enough that the partial writes and the
+// combine cost less than the idle CUs of the last round. The library splits when the
+// tail items would leave at least half of the CUs without work: with several resident
+// workgroups per CU, a last round that still reaches every CU is not slower in proportion
+// to its empty slots (fewer workgroups share each CU), and splitting it did not pay
+// (d = 64, a half-full round of three workgroups per CU: +1.6% time).
+constexpr int kTailMinTiles = 32;     // keys per item >= 2048 when the library chooses
+constexpr int kTailMaxParts = 16;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+template <int D, typename T, bool PRECISE>
+hipError_t plan_one(const PrefillParams& p, int kv_splits, PrefillPlan* plan) {
+  const Form f = choose_form<D, PRECISE>(p);
+  *plan = PrefillPlan{};
+  plan->items = f.items;
+  plan->rows = 32 * f.nw;
+  if constexpr (D > 128 || PRECISE) {
+    return hipSuccess;
+  } else {
+    const int n_tiles = (p.seqlen_k + kPage - 1) / kPage;
+    if (kv_splits == 1 || p.causal || f.ng != 1 || f.narrow || n_tiles == 0) return hipSuccess;
+    int occ = 1;
+    const hipError_t e = f.nw == 8 ? resident_per_cu<D, 8, T, PRECISE>(&occ) : resident_per_cu<D, 4, T, PRECISE>(&occ);
+    if (e != hipSuccess) return e;
+    const int64_t cap = (int64_t)occ * std::max(p.cus, 1);
+    const int64_t tail = f.items % cap;
+    if (tail == 0) return hipSuccess;
+    int64_t parts;
+    if (kv_splits >= 2) {
+      parts = kv_splits;
+    } else {
+      if (2 * tail > std::max(p.cus, 1) || n_tiles < kTailMinTiles) return hipSuccess;
+      parts = std::min<int64_t>({cap / tail, kTailMaxParts, n_tiles / 8});
+      if (parts < 2) return hipSuccess;
+    }
+    const int64_t rows = tail * plan->rows;
+    if (tail * parts > 0x7FFFFFFF || rows > 0x7FFFFFFF) return hipSuccess;
+    plan->parts = (int32_t)parts;
+    plan->tail = tail;
+    plan->part_o_off = 0;
+    plan->part_lse_off = align256((size_t)rows * parts * D * sizeof(float));
+    plan->row_off_off = plan->part_lse_off + align256((size_t)rows * parts * sizeof(float));
+    plan->row_lse_off = plan->row_off_off + align256((size_t)rows * sizeof(int64_t));
+    plan->bytes = plan->row_lse_off + align256((size_t)rows * sizeof(int64_t));
+    return hipSuccess;
+  }
+}
+
+template <int D, typename T, bool PRECISE>
+hipError_t launch_one(const PrefillParams& p0, const PrefillPlan& plan, hipStream_t stream) {
+  PrefillParams p = p0;
+  const Form f = choose_form<D, PRECISE>(p);
+  p.bq = f.bq;
+  p.split_parts = 0;
+  if constexpr (D == 256 && !PRECISE) {
+    if (f.blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_narrow_kernel<D, T>), dim3((unsigned)f.blocks), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  } else {
+    if constexpr (D <= 128) {
+      if (f.ng == 2) {
+        return f.pair ? launch_ng<D, 2, 4, T, PRECISE, true>(p, f.blocks, stream)
+                      : launch_ng<D, 2, 4, T, PRECISE>(p, f.blocks, stream);
+      }
+    }
+    auto launch1 = [&](const PrefillParams& q, int64_t blocks) -> hipError_t {
+      if constexpr (D <= 128) {
+        if (f.nw == 8) return launch_ng<D, 1, 8, T, PRECISE>(q, blocks, stream);
+      }
+      return launch_ng<D, 1, 4, T, PRECISE>(q, blocks, stream);
+    };
+    if (plan.parts < 2) return launch1(p, f.blocks);
+    // Tail split: the items before the tail as usual, then (item, part) units of the tail
+    // items writing partials, then the log-sum-exp combine of those partials into o.
+    const int64_t n_main = f.items - plan.tail;
+    if (n_main > 0) {
+      if (hipError_t e = launch1(p, n_main); e != hipSuccess) return e;
+    }
+    PrefillParams q = p;
+    q.split_parts = plan.parts;
+    q.split_item0 = (int32_t)n_main;
+    if (hipError_t e = launch1(q, plan.tail * plan.parts); e != hipSuccess) return e;
+    CombineParams c{};
+    c.part_o = p.part_o; c.part_lse = p.part_lse; c.o = p.o; c.lse = p.lse;
+    c.pairs = (int32_t)(plan.tail * plan.rows); c.num_splits = plan.parts;
+    c.o_dtype = p.o_dtype; c.o_round = p.o_round;
+    c.row_off = p.row_off; c.row_lse = p.row_lse;
+    return launch_combine(c, D, stream);
+  }
 }
 
 template <int D>
-hipError_t launch_d(const PrefillParams& p, int qkv_dtype, bool precise, hipStream_t s) {
+hipError_t plan_d(const PrefillParams& p, int qkv_dtype, bool precise, int kv_splits, PrefillPlan* plan) {
   if (qkv_dtype == kF16)
-    return precise ? launch_one<D, F16, true>(p, s) : launch_one<D, F16, false>(p, s);
-  return precise ? launch_one<D, BF16, true>(p, s) : launch_one<D, BF16, false>(p, s);
+    return precise ? plan_one<D, F16, true>(p, kv_splits, plan) : plan_one<D, F16, false>(p, kv_splits, plan);
+  return precise ? plan_one<D, BF16, true>(p, kv_splits, plan) : plan_one<D, BF16, false>(p, kv_splits, plan);
+}
+
+template <int D>
+hipError_t launch_d(const PrefillParams& p, const PrefillPlan& plan, int qkv_dtype, bool precise, hipStream_t s) {
+  if (qkv_dtype == kF16)
+    return precise ? launch_one<D, F16, true>(p, plan, s) : launch_one<D, F16, false>(p, plan, s);
+  return precise ? launch_one<D, BF16, true>(p, plan, s) : launch_one<D, BF16, false>(p, plan, s);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, int qkv_dtype, bool precise,
-                          hipStream_t stream) {
+hipError_t plan_prefill(const PrefillParams& p, int head_dim, int qkv_dtype, bool precise, int kv_splits,
+                        PrefillPlan* plan) {
   switch (head_dim) {
-    case 64: return launch_d<64>(p, qkv_dtype, precise, stream);
-    case 128: return launch_d<128>(p, qkv_dtype, precise, stream);
-    case 256: return launch_d<256>(p, qkv_dtype, precise, stream);
+    case 64: return plan_d<64>(p, qkv_dtype, precise, kv_splits, plan);
+    case 128: return plan_d<128>(p, qkv_dtype, precise, kv_splits, plan);
+    case 256: return plan_d<256>(p, qkv_dtype, precise, kv_splits, plan);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, int head_dim, int qkv_dtype,
+                          bool precise, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_d<64>(p, plan, qkv_dtype, precise, stream);
+    case 128: return launch_d<128>(p, plan, qkv_dtype, precise, stream);
+    case 256: return launch_d<256>(p, plan, qkv_dtype, precise, stream);
     default: return hipErrorInvalidValue;
   }
 }

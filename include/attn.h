@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 #define ATTN_PAGE_SIZE 64      /* tokens per KV page (block_size); equal to the KV tile width */
 #define ATTN_MAX_SPLITS 64     /* upper bound of num_splits for the split-KV decode */
 #define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)  /* scratch of attn_decode_fwd_noalloc: 32 MiB */
@@ -112,11 +112,36 @@ typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
  * L_b - S_q,b (a batch of chunked-prefill steps of different lengths). lse, when
  * given, is fp32 [Hq, total_q]. The caller sizes q, o and lse for total_q; the
  * library reads cu_seqlens_q only on the device.
+ * Tail split (the key-split of the last round of work, merged with a log-sum-exp
+ * combine: page "gfx942 unified attention, from the math up", section 8, and the
+ * 7minutos.es article on MoonMath AI's HIP attention kernel, paragraph "Punto de
+ * referencia"). The launch cuts the query rows into work items (256 or 128 rows of one
+ * sequence and KV head); when the last round of items on the device's CUs would leave
+ * CUs idle, the library can give the key tiles of each of those last items to several
+ * workgroups, which write fp32 partial outputs into the workspace, and merge the
+ * partials afterwards exactly as attn_splitkv_combine does. This is done only for
+ * non-causal launches with precise = 0 and d <= 128 (the items of such a launch all
+ * have the same key range). A split row's O is the same attention up to fp32 rounding
+ * and the fp16/bf16 rounding of P against a different running maximum: within the
+ * tolerances of the unsplit result, not bit-identical to it.
+ *  kv_splits  0: the library splits when the items of the last round would leave at
+ *             least half of the CUs idle and the items have at least 2048 keys (up to
+ *             16 parts); 1: never split;
+ *             2..ATTN_MAX_SPLITS: split the tail items into that many parts whenever
+ *             the last round is not full (every item when the launch has fewer items
+ *             than one round).
+ *  workspace, workspace_bytes  device scratch for the partials, 256-byte aligned, at
+ *             least attn_prefill_workspace_bytes(args) bytes; caller-owned and only
+ *             used in stream order by this call, so calls that may overlap need
+ *             separate workspaces. NULL (with workspace_bytes 0) turns the tail split
+ *             off when kv_splits = 0.
  * Errors: INVALID_ARG for null required pointers, misalignment, non-positive
  * sizes (B or S_q of 0 is a no-op returning OK), d not in {64,128,256}, a head
  * count that is not a multiple, a paged cache whose table cannot hold seqlen_k
  * keys (64*max_blocks_per_seq < seqlen_k), bad enum values, packed queries with the
- * BHSD layout or a misaligned cu_seqlens_q.
+ * BHSD layout or a misaligned cu_seqlens_q, kv_splits outside [0, ATTN_MAX_SPLITS],
+ * a split (kv_splits >= 2) without a workspace, or a workspace that is misaligned or
+ * smaller than attn_prefill_workspace_bytes(args).
  */
 typedef struct {
   const void* q;
@@ -142,9 +167,19 @@ typedef struct {
   int32_t precise;
   float scale;
   int32_t o_round;             /* attn_round_t for a bf16 output (0 = RTNE) */
+  int32_t kv_splits;           /* tail split: 0 = library's choice, 1 = never, n = n parts */
+  void* workspace;             /* tail split partials, or NULL */
+  size_t workspace_bytes;
 } attn_prefill_args_t;
 
 attn_status_t attn_prefill_fwd(const attn_prefill_args_t* args, void* stream);
+
+/* Bytes of workspace the call attn_prefill_fwd(args) uses for its tail split on the
+ * current device (0 when it does not split, including for arguments it would reject;
+ * the pointer fields of args are not read). Layout, each part 256-byte aligned: fp32
+ * partial outputs [rows, parts, d], fp32 partial lse [rows, parts], int64 output
+ * offsets [rows], int64 lse indices [rows], rows = tail items x rows per item. */
+size_t attn_prefill_workspace_bytes(const attn_prefill_args_t* args);
 
 /*
  * Split-KV decode (one query per sequence), split kernel + log-sum-exp combine.

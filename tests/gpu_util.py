@@ -49,7 +49,7 @@ def tolerance(case) -> float:
     return TOL_PRECISE if getattr(case, "precise", False) else TOL[case.dtype]
 
 
-def gpu_prefill(inp, *, with_lse=False, out_dtype=None, out_round="rtne"):
+def gpu_prefill(inp, *, with_lse=False, out_dtype=None, out_round="rtne", kv_splits=0):
     """Run attn_prefill_fwd on the seeded inputs; returns (O, lse) as float64 numpy.
 
     The output (and lse) buffers are filled with NaN before the launch and the whole
@@ -67,7 +67,7 @@ def gpu_prefill(inp, *, with_lse=False, out_dtype=None, out_round="rtne"):
     out = torch.full(q.shape, float("nan"), dtype=odt, device="cuda")
     o = attn_prefill_fwd(q, k, v, causal=c.causal, block_table=bt, seqlens_k=sl,
                          seqlen_k=c.seqlen_k, layout=c.layout, out=out, lse=lse,
-                         precise=c.precise, out_round=out_round)
+                         precise=c.precise, out_round=out_round, kv_splits=kv_splits)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()), "output rows left unwritten (NaN) or non-finite"
     if lse is not None:

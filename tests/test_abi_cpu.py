@@ -42,7 +42,8 @@ def test_header_constants_match_binding():
 
 def test_struct_sizes():
     # the ctypes mirrors must have the C layout (all fields naturally aligned, no padding holes)
-    assert ctypes.sizeof(_lib.PrefillArgs) == 8 * 8 + 15 * 4 + 4      # tail padding to 8
+    assert ctypes.sizeof(_lib.PrefillArgs) == 8 * 8 + 16 * 4 + 8 + 8   # workspace pointer and size last
+    assert _lib.PrefillArgs.workspace.offset == 128 and _lib.PrefillArgs.kv_splits.offset == 124
     assert ctypes.sizeof(_lib.DecodeArgs) == 8 * 8 + 8 + 12 * 4
     assert ctypes.sizeof(_lib.CombineArgs) == 4 * 8 + 6 * 4
     assert ctypes.sizeof(_lib.DeviceInfo) == 2 * 256 + 8 + 8 * 4
@@ -55,7 +56,8 @@ def prefill_args(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, block_table=FAKE, seqlens_k=FAKE, cu_seqlens_q=None,
              batch=1, num_heads_q=4, num_heads_kv=2, seqlen_q=128, seqlen_k=128, head_dim=128,
              num_blocks=2, max_blocks_per_seq=2, qkv_dtype=_lib.ATTN_F16, o_dtype=_lib.ATTN_F16,
-             layout=_lib.ATTN_BSHD, causal=1, precise=0, scale=0.0, o_round=_lib.ATTN_ROUND_RTNE)
+             layout=_lib.ATTN_BSHD, causal=1, precise=0, scale=0.0, o_round=_lib.ATTN_ROUND_RTNE,
+             kv_splits=0, workspace=None, workspace_bytes=0)
     a.update(kw)
     return _lib.PrefillArgs(**a)
 
@@ -95,6 +97,11 @@ BAD_PREFILL = [
     (dict(o_round=_lib.ATTN_ROUND_RTZ), _lib.ATTN_ERR_UNSUPPORTED, "fp16"),     # fp16 output
     (dict(cu_seqlens_q=FAKE, layout=_lib.ATTN_BHSD), _lib.ATTN_ERR_INVALID_ARG, "BSHD"),
     (dict(cu_seqlens_q=FAKE + 2), _lib.ATTN_ERR_INVALID_ARG, "cu_seqlens_q"),
+    (dict(kv_splits=-1), _lib.ATTN_ERR_INVALID_ARG, "kv_splits"),
+    (dict(kv_splits=65), _lib.ATTN_ERR_INVALID_ARG, "kv_splits"),
+    (dict(kv_splits=4), _lib.ATTN_ERR_INVALID_ARG, "needs a workspace"),
+    (dict(workspace=FAKE + 16, workspace_bytes=1 << 20), _lib.ATTN_ERR_INVALID_ARG, "256-byte"),
+    (dict(workspace_bytes=64), _lib.ATTN_ERR_INVALID_ARG, "without a workspace"),
 ]
 
 
@@ -117,6 +124,19 @@ def test_device_info_rejects_negative_index(lib):
     info = _lib.DeviceInfo()
     assert lib.attn_device_info(-1, ctypes.byref(info)) == _lib.ATTN_ERR_INVALID_ARG
     assert "device" in _lib.last_error()
+
+
+def test_prefill_workspace_query_without_device(lib):
+    # a size query: 0 for arguments the call would reject, for kv_splits = 1 and (here,
+    # with no device to plan on) for everything else; it leaves the last error alone
+    assert lib.attn_prefill_fwd(ctypes.byref(prefill_args(head_dim=96)), None) == _lib.ATTN_ERR_INVALID_ARG
+    before = _lib.last_error()
+    assert lib.attn_prefill_workspace_bytes(ctypes.byref(prefill_args(kv_splits=1, causal=0))) == 0
+    assert lib.attn_prefill_workspace_bytes(ctypes.byref(prefill_args(kv_splits=99))) == 0
+    assert lib.attn_prefill_workspace_bytes(None) == 0
+    if lib.attn_device_count() == 0:
+        assert lib.attn_prefill_workspace_bytes(ctypes.byref(prefill_args(kv_splits=4, causal=0))) == 0
+    assert _lib.last_error() == before
 
 
 def test_prefill_empty_is_noop(lib):

@@ -1,0 +1,147 @@
+"""GPU parity of the prefill tail split: the key tiles of the last work items are given
+to several workgroups whose fp32 partials the log-sum-exp combine merges (page "gfx942
+unified attention, from the math up", section 8; the 7minutos.es article on MoonMath
+AI's HIP attention kernel, paragraph "Punto de referencia"). Forced part counts on small
+shapes (every item is then in the tail) against the fp64 oracle, O and lse; the
+library's own choice on shapes whose last round is partly empty, in the four-wave and
+the eight-wave forms."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attn_workloads import PrefillCase, bits_to_f64, make_prefill_inputs
+from gpu_util import (check_bf16_rounding, dev, dev_i32, gpu_prefill, lse_tolerance, max_abs_err,
+                      oracle_prefill, say, to_f64, tolerance)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+P = PrefillCase
+FORCED = [
+    (P("split_bf16_d128_dense_ragged", 1, 2, 2, 300, 1000, 128, "bf16", False, "dense"), 3),
+    (P("split_f16_d64_gqa4_paged_empty_seq", 2, 8, 2, 200, 700, 64, "f16", False, "paged",
+       seqlens_k=(700, 0)), 5),
+    (P("split_bf16_d128_bhsd_f32out_empty_parts", 2, 4, 4, 130, 257, 128, "bf16", False, "dense",
+       layout="bhsd", out_dtype="f32"), 7),
+    (P("split_f16_d128_gqa8_64_parts", 1, 16, 2, 90, 150, 128, "f16", False, "paged"), 64),
+    (P("split_bf16_d64_cross_ragged", 3, 4, 1, 333, 65, 64, "bf16", False, "dense",
+       seqlens_k=(65, 1, 30)), 2),
+]
+
+
+def _workspace_bytes(case, kv_splits):
+    from attention_forward_tiled_amd import attn_prefill_workspace_bytes
+    shape = ((case.batch, case.seqlen_q, case.heads_q, case.head_dim) if case.layout == "bshd"
+             else (case.batch, case.heads_q, case.seqlen_q, case.head_dim))
+    q = torch.empty(shape, dtype={"f16": torch.float16, "bf16": torch.bfloat16}[case.dtype], device="cuda")
+    return attn_prefill_workspace_bytes(q, num_heads_kv=case.heads_kv, seqlen_k=case.seqlen_k,
+                                        causal=case.causal, layout=case.layout, kv_splits=kv_splits)
+
+
+@pytest.mark.parametrize("case,parts", FORCED, ids=lambda x: getattr(x, "name", str(x)))
+def test_tail_split_forced(case, parts):
+    say(f"tail split parity {case.name}, {parts} parts")
+    assert _workspace_bytes(case, parts) > 0, "the launch does not split"
+    inp = make_prefill_inputs(case, seed=5)
+    O, lse = gpu_prefill(inp, with_lse=True, kv_splits=parts)
+    Oref, lref = oracle_prefill(inp)
+    err = max_abs_err(O, Oref)
+    say(f"  max abs err {err:.3e} (tol {tolerance(case)})")
+    assert err <= tolerance(case)
+    fin = np.isfinite(lref)
+    assert (np.isneginf(lse) == ~fin).all()
+    assert np.abs(lse[fin] - lref[fin]).max(initial=0.0) <= lse_tolerance(case.dtype)
+    # the same launch unsplit: both within the tolerance of the oracle, so within twice it
+    # of each other; rows with no key are exactly zero in both
+    O1, _ = gpu_prefill(inp, with_lse=True, kv_splits=1)
+    assert max_abs_err(O, O1) <= 2 * tolerance(case)
+    empty = ~fin if case.layout == "bhsd" else (~fin).transpose(0, 2, 1)    # over O's first 3 axes
+    assert (O[empty] == 0).all() and (O1[empty] == 0).all()
+
+
+@pytest.mark.parametrize("mode", ["rtne", "rtna", "rtz"])
+def test_tail_split_bf16_output_rounding(mode):
+    # the combine rounds the merged fp32 row: the bf16 output of a split launch relates to
+    # the fp32 output of the same split launch as the rounding mode says
+    case = P("split_bf16_d128_round", 2, 4, 2, 160, 600, 128, "bf16", False, "dense")
+    say(f"tail split bf16 output rounding {mode}")
+    inp = make_prefill_inputs(case, seed=6)
+    O32, _ = gpu_prefill(inp, out_dtype="f32", kv_splits=4)
+    O16, _ = gpu_prefill(inp, out_round=mode, kv_splits=4)
+    check_bf16_rounding(O16, O32, mode)
+
+
+def test_tail_split_packed_queries():
+    from attention_forward_tiled_amd import attn_prefill_fwd
+    case = P("split_bf16_d128_packed_gqa2", 3, 4, 2, 300, 800, 128, "bf16", False, "paged",
+             seqlens_k=(800, 65, 300))
+    q_lens = (300, 0, 129)
+    say(f"tail split parity, packed queries {case.name} q_lens={q_lens}")
+    inp = make_prefill_inputs(case, seed=7)
+    c = case
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q = dev(np.concatenate([inp.q[b, :n] for b, n in enumerate(q_lens)], axis=0), c.dtype)
+    k, v = dev(inp.k, c.dtype), dev(inp.v, c.dtype)
+    lse = torch.full((c.heads_q, int(cu[-1])), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    attn_prefill_fwd(q, k, v, causal=False, block_table=dev_i32(inp.block_table),
+                     seqlens_k=dev_i32(inp.seqlens_k), seqlen_k=c.seqlen_k, cu_seqlens_q=dev_i32(cu),
+                     max_seqlen_q=c.seqlen_q, lse=lse, out=out, kv_splits=6)
+    torch.cuda.synchronize()
+    O, L = to_f64(out), to_f64(lse)
+    assert np.isfinite(O).all() and not np.isnan(L).any()
+    qf, kf, vf = (bits_to_f64(x, c.dtype) for x in (inp.q, inp.k, inp.v))
+    for b, n in enumerate(q_lens):
+        if n == 0:
+            continue
+        Oref, lref = oracle.attention(qf[b:b + 1, :n], kf, vf, causal=False,
+                                      block_table=inp.block_table[b:b + 1], seqlens_k=inp.seqlens_k[b:b + 1])
+        rows = slice(int(cu[b]), int(cu[b + 1]))
+        err = max_abs_err(O[rows], Oref[0])
+        say(f"  sequence {b}: {n} queries, max abs err {err:.3e}")
+        assert err <= tolerance(case)
+        assert np.abs(L[:, rows] - lref[0]).max() <= lse_tolerance(c.dtype)
+
+
+def _sampled_check(case, inp, O, rows_of):
+    """Oracle on chosen query rows of every (sequence, head) of a dense BSHD case."""
+    inp_q, inp_k, inp_v, d, G = inp.q, inp.k, inp.v, case.head_dim, case.group
+    worst = 0.0
+    for b in range(case.batch):
+        for h in range(case.heads_q):
+            rows = rows_of(b, h)
+            K = bits_to_f64(inp_k[b, :, h // G, :], case.dtype)
+            V = bits_to_f64(inp_v[b, :, h // G, :], case.dtype)
+            Oref, _ = oracle.attention_rows(bits_to_f64(inp_q[b, rows, h, :], case.dtype), K, V, rows,
+                                            case.seqlen_k, case.seqlen_q, False, 1.0 / np.sqrt(d))
+            worst = max(worst, max_abs_err(O[b, rows, h, :], Oref))
+    return worst
+
+
+AUTO = [
+    # four-wave form: 32 items of 128 rows, fewer than one round -> every item split
+    P("auto_bf16_d128_s1024x4096", 1, 4, 4, 1024, 4096, 128, "bf16", False, "dense", poison=False),
+    # eight-wave form: 17 KV heads x 64 query blocks = 1088 items of 256 rows, the last
+    # 64 (one whole head) in a quarter-full round -> split
+    P("auto_f16_d128_h17_s16384x2048_wg8", 1, 17, 17, 16384, 2048, 128, "f16", False, "dense", poison=False),
+]
+
+
+@pytest.mark.parametrize("case", AUTO, ids=lambda c: c.name)
+def test_tail_split_library_choice(case):
+    say(f"tail split chosen by the library {case.name}")
+    assert _workspace_bytes(case, 0) > 0, "the library does not split this launch"
+    inp = make_prefill_inputs(case, seed=8)
+    O, _ = gpu_prefill(inp, kv_splits=0)
+    O1, _ = gpu_prefill(inp, kv_splits=1)
+    diff = max_abs_err(O, O1)
+    say(f"  split vs unsplit max abs diff {diff:.3e}")
+    assert diff <= 2 * tolerance(case)
+    rng = np.random.default_rng(8)
+    S = case.seqlen_q
+    # one seeded row per 32-row slice (every wave of every workgroup, split or not)
+    worst = _sampled_check(case, inp, O, lambda b, h: np.minimum(
+        np.arange(0, S, 32) + rng.integers(0, 32, -(-S // 32)), S - 1))
+    say(f"  max abs err {worst:.3e} (tol {tolerance(case)})")
+    assert worst <= tolerance(case)
