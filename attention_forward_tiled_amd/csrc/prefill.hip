@@ -552,8 +552,12 @@ void prefill_narrow_kernel(const PrefillParams p) {
   const int nx = gridDim.x, xcd = blockIdx.x & 7, per = nx >> 3, extra = nx & 7;
   const int lid = xcd * per + min(xcd, extra) + (int)(blockIdx.x >> 3);
   const int nq = (p.seqlen_q + p.bq - 1) / p.bq;
-  const int unit = lid % nq;
-  const int bh = lid / nq;
+  // tail split: `lid` numbers (item, key part) units, as in prefill_kernel
+  const int nsp = p.split_parts;
+  const int item = nsp ? p.split_item0 + lid / nsp : lid;
+  const int part = nsp ? lid % nsp : 0;
+  const int unit = item % nq;
+  const int bh = item / nq;
   const int b = bh % p.batch, kvh = bh / p.batch;
 
   int L = p.seqlen_k;
@@ -588,6 +592,13 @@ void prefill_narrow_kernel(const PrefillParams p) {
   int n_full = L / kPage;
   if (p.causal) n_full = min(n_full, max(q0 + off + 1, 0) / kPage);
   n_full = min(n_full, n_tiles);
+  // key tiles [j0, j1) of this workgroup: all of them, or one part of a tail split
+  int j0 = 0, j1 = n_tiles;
+  if (nsp) {
+    const int tp = (n_tiles + nsp - 1) / nsp;
+    j0 = min(part * tp, n_tiles);
+    j1 = min(n_tiles, j0 + tp);
+  }
 
   const bool paged = p.block_table != nullptr;
   const int64_t rs = paged ? (int64_t)p.hkv * D : p.kv_ss;
@@ -724,40 +735,60 @@ void prefill_narrow_kernel(const PrefillParams p) {
 
   using Full = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
-  auto step = [&](int j, auto stage_c, auto mask_c) {
+  // step i takes tile j0 + i from stage i % 2
+  auto step = [&](int i, auto stage_c, auto mask_c) {
     constexpr int STAGE = decltype(stage_c)::value;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    if (j + 1 < n_tiles) issue_tile(j + 1, STAGE ^ 1);
+    const int j = j0 + i;
+    if (j + 1 < j1) issue_tile(j + 1, STAGE ^ 1);
     if ((stage_ok >> STAGE) & 1u) compute(j, stage_c, mask_c);
   };
-  // tiles [0, n_full) need no mask, [n_full, n_tiles) do: two loops, so that each loop
-  // body holds one kind of tile (one register assignment for the loop-carried state)
-  if (n_tiles > 0) issue_tile(0, 0);
-  int j = 0;
-  for (; j + 1 < n_full; j += 2) {
-    step(j, std::integral_constant<int, 0>{}, Full{});
-    step(j + 1, std::integral_constant<int, 1>{}, Full{});
+  // tiles below n_full need no mask, the others do: two loops, so that each loop body
+  // holds one kind of tile (one register assignment for the loop-carried state)
+  const int h = j1 - j0, nf = max(0, min(n_full, j1) - j0);
+  if (h > 0) issue_tile(j0, 0);
+  int i = 0;
+  for (; i + 1 < nf; i += 2) {
+    step(i, std::integral_constant<int, 0>{}, Full{});
+    step(i + 1, std::integral_constant<int, 1>{}, Full{});
   }
-  if (j < n_full) {
-    step(j, std::integral_constant<int, 0>{}, Full{});
-    ++j;
+  if (i < nf) {
+    step(i, std::integral_constant<int, 0>{}, Full{});
+    ++i;
   }
-  // the masked loop is unrolled by two as well (the stage of tile j is j % 2): a loop whose
-  // body picks one of two stage bodies at run time spills 84 registers here
-  if (j < n_tiles && (j & 1)) {
-    step(j, std::integral_constant<int, 1>{}, Masked{});
-    ++j;
+  // the masked loop is unrolled by two as well: a loop whose body picks one of two stage
+  // bodies at run time spills 84 registers here
+  if (i < h && (i & 1)) {
+    step(i, std::integral_constant<int, 1>{}, Masked{});
+    ++i;
   }
-  for (; j + 1 < n_tiles; j += 2) {
-    step(j, std::integral_constant<int, 0>{}, Masked{});
-    step(j + 1, std::integral_constant<int, 1>{}, Masked{});
+  for (; i + 1 < h; i += 2) {
+    step(i, std::integral_constant<int, 0>{}, Masked{});
+    step(i + 1, std::integral_constant<int, 1>{}, Masked{});
   }
-  if (j < n_tiles) step(j, std::integral_constant<int, 0>{}, Masked{});
+  if (i < h) step(i, std::integral_constant<int, 0>{}, Masked{});
 
   // ---- epilogue: lane holds d = 16 db + 4 lg + i of its row
   const float l = rows4_sum(lsum);
-  if (rok) {
+  if (nsp) {
+    // tail split: this part's normalised O and lse in fp32, for the combine; part 0 also
+    // records where the row goes (-1 for a padding row)
+    const int64_t prow = (int64_t)(lid / nsp) * (16 * NW) + wave * 16 + lr;
+    if (rok) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* po = p.part_o + (prow * nsp + part) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<float4v*>(po + 16 * db + 4 * lg) = acc[db] * inv;
+      if (lg == 0) p.part_lse[prow * nsp + part] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+    }
+    if (lg == 0 && part == 0) {
+      p.row_off[prow] = rok ? b * p.o_sb + (int64_t)rh * p.o_sh + (qrow0 + rpos) * p.o_ss : -1;
+      p.row_lse[prow] = !(rok && p.lse) ? -1
+                        : p.cu_seqlens_q ? (int64_t)rh * scalar_load(p.cu_seqlens_q + p.batch) + qrow0 + rpos
+                                         : ((int64_t)b * p.hq + rh) * p.seqlen_q + rpos;
+    }
+  } else if (rok) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t ob = b * p.o_sb + (int64_t)rh * p.o_sh + (qrow0 + rpos) * p.o_ss;
 #pragma unroll
@@ -845,9 +876,10 @@ Form choose_form(const PrefillParams& p) {
   return f;
 }
 
-// Workgroups of one-group form NW that stay resident on a CU at once (registers and LDS
-// of the compiled kernel), asked once per kernel.
-template <int D, int NW, typename T, bool PRECISE>
+// Workgroups of a kernel that stay resident on a CU at once (registers and LDS of the
+// compiled kernel), asked once per kernel: the one-group form of NW waves, or (NW = 0) the
+// narrow d = 256 kernel.
+template <int D, int NW, typename T>
 hipError_t resident_per_cu(int* n) {
   static int cached = 0;
   if (cached > 0) {
@@ -855,8 +887,14 @@ hipError_t resident_per_cu(int* n) {
     return hipSuccess;
   }
   int v = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &v, reinterpret_cast<const void*>(&prefill_kernel<D, 1, NW, T, PRECISE, false>), 64 * NW, 0);
+  hipError_t e;
+  if constexpr (NW == 0) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &v, reinterpret_cast<const void*>(&prefill_narrow_kernel<D, T>), 512, 0);
+  } else {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &v, reinterpret_cast<const void*>(&prefill_kernel<D, 1, NW, T, false, false>), 64 * NW, 0);
+  }
   if (e != hipSuccess) return e;
   cached = std::max(v, 1);
   *n = cached;
@@ -880,14 +918,16 @@ hipError_t plan_one(const PrefillParams& p, int kv_splits, PrefillPlan* plan) {
   const Form f = choose_form<D, PRECISE>(p);
   *plan = PrefillPlan{};
   plan->items = f.items;
-  plan->rows = 32 * f.nw;
-  if constexpr (D > 128 || PRECISE) {
+  plan->rows = (f.narrow ? 16 : 32) * f.nw;
+  if constexpr (PRECISE) {
     return hipSuccess;
   } else {
     const int n_tiles = (p.seqlen_k + kPage - 1) / kPage;
-    if (kv_splits == 1 || p.causal || f.ng != 1 || f.narrow || n_tiles == 0) return hipSuccess;
+    if (kv_splits == 1 || p.causal || f.ng != 1 || n_tiles == 0) return hipSuccess;
     int occ = 1;
-    const hipError_t e = f.nw == 8 ? resident_per_cu<D, 8, T, PRECISE>(&occ) : resident_per_cu<D, 4, T, PRECISE>(&occ);
+    hipError_t e;
+    if constexpr (D == 256) e = resident_per_cu<D, 0, T>(&occ);
+    else e = f.nw == 8 ? resident_per_cu<D, 8, T>(&occ) : resident_per_cu<D, 4, T>(&occ);
     if (e != hipSuccess) return e;
     const int64_t cap = (int64_t)occ * std::max(p.cus, 1);
     const int64_t tail = f.items % cap;
@@ -919,41 +959,42 @@ hipError_t launch_one(const PrefillParams& p0, const PrefillPlan& plan, hipStrea
   const Form f = choose_form<D, PRECISE>(p);
   p.bq = f.bq;
   p.split_parts = 0;
-  if constexpr (D == 256 && !PRECISE) {
-    if (f.blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_narrow_kernel<D, T>), dim3((unsigned)f.blocks), dim3(512), 0, stream, p);
-    return hipGetLastError();
-  } else {
-    if constexpr (D <= 128) {
-      if (f.ng == 2) {
-        return f.pair ? launch_ng<D, 2, 4, T, PRECISE, true>(p, f.blocks, stream)
-                      : launch_ng<D, 2, 4, T, PRECISE>(p, f.blocks, stream);
-      }
-    }
-    auto launch1 = [&](const PrefillParams& q, int64_t blocks) -> hipError_t {
+  // one launch of the chosen one-group kernel over `blocks` workgroups
+  auto launch1 = [&](const PrefillParams& q, int64_t blocks) -> hipError_t {
+    if constexpr (D == 256 && !PRECISE) {
+      if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((prefill_narrow_kernel<D, T>), dim3((unsigned)blocks), dim3(512), 0, stream, q);
+      return hipGetLastError();
+    } else {
       if constexpr (D <= 128) {
         if (f.nw == 8) return launch_ng<D, 1, 8, T, PRECISE>(q, blocks, stream);
       }
       return launch_ng<D, 1, 4, T, PRECISE>(q, blocks, stream);
-    };
-    if (plan.parts < 2) return launch1(p, f.blocks);
-    // Tail split: the items before the tail as usual, then (item, part) units of the tail
-    // items writing partials, then the log-sum-exp combine of those partials into o.
-    const int64_t n_main = f.items - plan.tail;
-    if (n_main > 0) {
-      if (hipError_t e = launch1(p, n_main); e != hipSuccess) return e;
     }
-    PrefillParams q = p;
-    q.split_parts = plan.parts;
-    q.split_item0 = (int32_t)n_main;
-    if (hipError_t e = launch1(q, plan.tail * plan.parts); e != hipSuccess) return e;
-    CombineParams c{};
-    c.part_o = p.part_o; c.part_lse = p.part_lse; c.o = p.o; c.lse = p.lse;
-    c.pairs = (int32_t)(plan.tail * plan.rows); c.num_splits = plan.parts;
-    c.o_dtype = p.o_dtype; c.o_round = p.o_round;
-    c.row_off = p.row_off; c.row_lse = p.row_lse;
-    return launch_combine(c, D, stream);
+  };
+  if constexpr (D <= 128) {
+    if (f.ng == 2) {
+      return f.pair ? launch_ng<D, 2, 4, T, PRECISE, true>(p, f.blocks, stream)
+                    : launch_ng<D, 2, 4, T, PRECISE>(p, f.blocks, stream);
+    }
   }
+  if (plan.parts < 2) return launch1(p, f.blocks);
+  // Tail split: the items before the tail as usual, then (item, part) units of the tail
+  // items writing partials, then the log-sum-exp combine of those partials into o.
+  const int64_t n_main = f.items - plan.tail;
+  if (n_main > 0) {
+    if (hipError_t e = launch1(p, n_main); e != hipSuccess) return e;
+  }
+  PrefillParams q = p;
+  q.split_parts = plan.parts;
+  q.split_item0 = (int32_t)n_main;
+  if (hipError_t e = launch1(q, plan.tail * plan.parts); e != hipSuccess) return e;
+  CombineParams c{};
+  c.part_o = p.part_o; c.part_lse = p.part_lse; c.o = p.o; c.lse = p.lse;
+  c.pairs = (int32_t)(plan.tail * plan.rows); c.num_splits = plan.parts;
+  c.o_dtype = p.o_dtype; c.o_round = p.o_round;
+  c.row_off = p.row_off; c.row_lse = p.row_lse;
+  return launch_combine(c, D, stream);
 }
 
 template <int D>

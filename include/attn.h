@@ -120,8 +120,8 @@ typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
  * CUs idle, the library can give the key tiles of each of those last items to several
  * workgroups, which write fp32 partial outputs into the workspace, and merge the
  * partials afterwards exactly as attn_splitkv_combine does. This is done only for
- * non-causal launches with precise = 0 and d <= 128 (the items of such a launch all
- * have the same key range). A split row's O is the same attention up to fp32 rounding
+ * non-causal launches with precise = 0 (the items of such a launch all have the same
+ * key range). A split row's O is the same attention up to fp32 rounding
  * and the fp16/bf16 rounding of P against a different running maximum: within the
  * tolerances of the unsplit result, not bit-identical to it.
  *  kv_splits  0: the library splits when the items of the last round would leave at

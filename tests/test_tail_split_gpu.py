@@ -3,8 +3,8 @@ to several workgroups whose fp32 partials the log-sum-exp combine merges (page "
 unified attention, from the math up", section 8; the 7minutos.es article on MoonMath
 AI's HIP attention kernel, paragraph "Punto de referencia"). Forced part counts on small
 shapes (every item is then in the tail) against the fp64 oracle, O and lse; the
-library's own choice on shapes whose last round is partly empty, in the four-wave and
-the eight-wave forms."""
+library's own choice on shapes whose last round is partly empty, in the four-wave, the
+eight-wave and the d = 256 narrow forms."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +27,10 @@ FORCED = [
     (P("split_f16_d128_gqa8_64_parts", 1, 16, 2, 90, 150, 128, "f16", False, "paged"), 64),
     (P("split_bf16_d64_cross_ragged", 3, 4, 1, 333, 65, 64, "bf16", False, "dense",
        seqlens_k=(65, 1, 30)), 2),
+    # d = 256: the eight-wave narrow kernel (16 rows per wave, 128 per item)
+    (P("split_bf16_d256_dense_ragged", 2, 2, 2, 200, 700, 256, "bf16", False, "dense"), 3),
+    (P("split_f16_d256_gqa2_paged_varlen_f32out", 2, 4, 2, 130, 500, 256, "f16", False, "paged",
+       seqlens_k=(500, 64), out_dtype="f32"), 5),
 ]
 
 
@@ -125,6 +129,8 @@ AUTO = [
     # eight-wave form: 17 KV heads x 64 query blocks = 1088 items of 256 rows, the last
     # 64 (one whole head) in a quarter-full round -> split
     P("auto_f16_d128_h17_s16384x2048_wg8", 1, 17, 17, 16384, 2048, 128, "f16", False, "dense", poison=False),
+    # d = 256 narrow kernel: 5 heads x 64 query blocks = 320 items, the last 64 split
+    P("auto_bf16_d256_h5_s8192x4096", 1, 5, 5, 8192, 4096, 256, "bf16", False, "dense", poison=False),
 ]
 
 
