@@ -123,6 +123,12 @@ CONFIGS = {
         seqlen_k=4096, head_dim=64, dtype="f16", causal=True, kv="dense", layout="bshd",
         poison=False),
     # Long non-causal MHA self-attention, dense BSHD K/V, inputs 0.5*N(0,1).
+    # A launch whose last round of work items is a quarter full (25 heads x 64 query
+    # blocks of 256 rows on 256 CUs): the shape of the prefill tail split.
+    "tail_noncausal_bf16_h25_s16384": PrefillCase(
+        "tail_noncausal_bf16_h25_s16384", batch=1, heads_q=25, heads_kv=25, seqlen_q=16384,
+        seqlen_k=16384, head_dim=128, dtype="bf16", causal=False, kv="dense",
+        layout="bshd", value_scale=0.5, poison=False),
     "long_noncausal_bf16_s16384": PrefillCase(
         "long_noncausal_bf16_s16384", batch=4, heads_q=16, heads_kv=16, seqlen_q=16384,
         seqlen_k=16384, head_dim=128, dtype="bf16", causal=False, kv="dense",

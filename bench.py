@@ -150,14 +150,23 @@ class PrefillWorkload:
         self.sl = torch.from_numpy(self.inp.seqlens_k).cuda() if need_lens else None
         odt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[case.o_dtype]
         self.out = torch.full(self.q.shape, float("nan"), dtype=odt, device="cuda")
+        # workspace of the tail split, when the library splits this launch (allocated
+        # once, outside the timed region); the step is then main items, split units and
+        # the combine
+        from attention_forward_tiled_amd import attn_prefill_workspace_bytes
+        need = attn_prefill_workspace_bytes(self.q, num_heads_kv=case.heads_kv, seqlen_k=case.seqlen_k,
+                                            causal=case.causal, layout=case.layout, precise=case.precise)
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        self.tail_split_bytes = need
 
     def step(self):
         c = self.case
         self.fn(self.q, self.k, self.v, causal=c.causal, block_table=self.bt, seqlens_k=self.sl,
-                seqlen_k=c.seqlen_k, layout=c.layout, out=self.out, precise=c.precise)
+                seqlen_k=c.seqlen_k, layout=c.layout, out=self.out, precise=c.precise,
+                kv_splits=0 if self.ws is not None else 1, workspace=self.ws)
 
     def kernel_only(self):
-        return None          # one kernel per step: the step is the kernel
+        return None          # the step is the prefill launch (three kernels with a tail split)
 
     def work(self):
         return float(self.case.flops_half_convention())
@@ -171,7 +180,8 @@ class PrefillWorkload:
                 "seqlen_q": c.seqlen_q, "seqlen_k": c.seqlen_k, "head_dim": c.head_dim,
                 "causal": c.causal, "kv": c.kv, "layout": c.layout, "dtype": c.dtype,
                 "flops_per_step": self.work(), "flops_exact_per_step": float(c.flops_exact()),
-                "flop_convention": "4*d*S_q*S_k*B*Hq, halved when causal"}
+                "flop_convention": "4*d*S_q*S_k*B*Hq, halved when causal",
+                "tail_split_workspace_bytes": int(self.tail_split_bytes)}
 
     def sample_rows(self):
         Sq = self.case.seqlen_q

@@ -185,3 +185,57 @@ def test_packed_prefill_graph_new_offsets():
             Oref, _ = oracle.attention(qf[None, rows], kf, vf, causal=True,
                                        block_table=inp.block_table[b:b + 1], seqlens_k=inp.seqlens_k[b:b + 1])
             assert max_abs_err(O[rows], Oref[0]) <= tolerance(case)
+
+
+def test_prefill_tail_split_graph_replays():
+    """A tail-split call (main items, split units, combine: three kernels) with its
+    workspace passed in, captured once and replayed with new queries and key lengths."""
+    from attention_forward_tiled_amd import attn_prefill_fwd, attn_prefill_workspace_bytes
+    case = PrefillCase("graph_bf16_d128_split_paged", 2, 8, 2, 300, 900, 128, "bf16", False, "paged",
+                       seqlens_k=(900, 640))
+    say(f"prefill tail-split graph capture, {case}")
+    inp = make_prefill_inputs(case, seed=24)
+    q = dev(inp.q, case.dtype)
+    k, v = dev(inp.k, case.dtype), dev(inp.v, case.dtype)
+    bt, sl = dev_i32(inp.block_table), dev_i32(inp.seqlens_k)
+    need = attn_prefill_workspace_bytes(q, num_heads_kv=case.heads_kv, seqlen_k=case.seqlen_k, causal=False,
+                                        kv_splits=4)
+    assert need > 0, "the launch does not split"
+    ws, ws_eager = (torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2))
+
+    def run(o, lse, w):
+        attn_prefill_fwd(q, k, v, causal=False, block_table=bt, seqlens_k=sl, seqlen_k=case.seqlen_k,
+                         out=o, lse=lse, kv_splits=4, workspace=w)
+
+    out = torch.empty_like(q)
+    lse = torch.empty((case.batch, case.heads_q, case.seqlen_q), dtype=torch.float32, device="cuda")
+    run(out, lse, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(out, lse, ws)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(9)
+    lens, qbits = inp.seqlens_k, inp.q
+    for i in range(REPLAYS):
+        if i > 0:
+            qbits = make_prefill_inputs(case, seed=300 + i).q
+            q.copy_(dev(qbits, case.dtype))
+            lens = shorter_lengths(inp.seqlens_k, rng)
+            sl.copy_(dev_i32(lens))
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        ref_o, ref_l = torch.empty_like(out), torch.empty_like(lse)
+        run(ref_o, ref_l, ws_eager)
+        torch.cuda.synchronize()
+        say(f"  replay {i}: lengths {lens.tolist()}")
+        assert same_bits(out, ref_o) and same_bits(lse, ref_l), f"replay {i} differs from the eager call"
+        if i in (0, REPLAYS - 1):
+            Oref, lref = oracle.attention(bits_to_f64(qbits, case.dtype), bits_to_f64(inp.k, case.dtype),
+                                          bits_to_f64(inp.v, case.dtype), causal=False,
+                                          block_table=inp.block_table, seqlens_k=lens)
+            assert max_abs_err(to_f64(out), Oref) <= tolerance(case)
+            assert (np.isneginf(to_f64(lse)) == np.isneginf(lref)).all()
