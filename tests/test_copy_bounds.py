@@ -11,7 +11,8 @@ source must lie inside its buffer (or be the zero chunk), every table read insid
 table, every store inside its output, and the 32-bit per-lane byte offsets must not
 overflow. The composition of the 64-bit copy base from two wave-uniform halves is
 checked for addresses whose low word has bit 31 set (the case a sign extension gets
-wrong). Nothing here runs on a GPU.
+wrong). The tail split's two launches and combine are modelled too (unit -> item and
+key part, partial slots, row map). Nothing here runs on a GPU.
 """
 import math
 
@@ -225,6 +226,126 @@ def test_prefill_packed_query_addresses_in_bounds():
     cu = np.array([0, 100, 100, 357, 421])
     check_prefill(128, 4, 8, 2, 257, 1000, True, True, lens=(300, 50, 200, 1000), cu=cu)
     check_prefill(64, 3, 4, 4, 200, 130, False, False, lens=(130, 7, 130), cu=np.array([0, 33, 233, 234]))
+
+
+def check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged=False, lens=None):
+    """The tail split of a non-causal one-group launch (plan_one / launch_one and the
+    split mode of both prefill kernels): the main launch takes items [0, N - tail), the
+    split launch's unit u (through the same XCD permutation) takes part u % parts of item
+    N - tail + u / parts; partial rows, partial slots and row-map entries stay inside the
+    workspace the plan sizes; part 0 writes every row-map entry once; together the two
+    launches own every query row exactly once; the combine reads only inside the
+    partials."""
+    G = Hq // Hkv
+    NG, NW, PAIR, bq = prefill_form(D, False, G, Sq, Sk, B, Hkv)
+    assert NG == 1 and not PAIR
+    R = 16 * 8 if D == 256 else 32 * NW            # rows per item (narrow: 8 waves x 16)
+    assert R == NW * 32                            # the same rows as the four-wave model
+    lens = np.full(B, Sk) if lens is None else np.asarray(lens)
+    nq = -(-Sq // bq)
+    N = nq * Hkv * B
+    assert 0 < tail <= N and 2 <= parts <= 64
+    q_sb, q_sh, q_ss = Sq * Hq * D, D, Hq * D
+    kv_sb, kv_sh, kv_ss = Sk * Hkv * D, D, Hkv * D
+    pages_per_seq = -(-Sk // PAGE)
+    if paged:
+        num_blocks = B * pages_per_seq
+        table = np.random.default_rng(1).permutation(num_blocks).reshape(B, pages_per_seq)
+        kv_elems, rs = num_blocks * PAGE * Hkv * D, Hkv * D
+    else:
+        kv_elems, rs = B * Sk * Hkv * D, kv_ss
+    o_elems = B * Sq * Hq * D
+    rows = tail * R                                # workspace layout of the plan
+    part_o_elems, part_lse_elems = rows * parts * D, rows * parts
+    owned = np.zeros((B, Hq, Sq), dtype=np.int64)
+    row_map = np.full(rows, -2, dtype=np.int64)    # -2: never written
+    rows_w = np.arange(R)
+
+    def item_rows(item):
+        unit, bh = item % nq, item // nq
+        b, kvh = bh % B, bh // B
+        q0 = (nq - 1 - unit) * bq
+        hig = rows_w // bq
+        rpos = q0 + (rows_w - hig * bq)
+        rh = kvh * G + hig
+        rok = (hig < G) & (rpos < Sq)
+        L = min(max(int(lens[b]), 0), Sk)
+        n_tiles = (L + PAGE - 1) // PAGE if (L > 0 and q0 < Sq) else 0
+        return b, kvh, rh, rpos, rok, L, n_tiles
+
+    def copy_tiles(b, kvh, L, j0, j1):
+        for j in range(j0, j1):
+            if paged:
+                pg = int(table[b, j])
+                base = pg * PAGE * Hkv * D + kvh * D
+            else:
+                base = b * kv_sb + kvh * kv_sh + j * PAGE * kv_ss
+            full = (j + 1) * PAGE <= L
+            row_ok = np.full(PAGE, full) if full else np.array([j * PAGE + r < L for r in range(PAGE)])
+            o, z, dma = tile_sources(D, swz_prefill, base, rs, row_ok)
+            assert dma.max() < 2 ** 32
+            assert_inside(o, z, kv_elems, f"tail-split tile b={b} kvh={kvh} j={j}")
+
+    def xcd_lid(bx, nx):
+        per, extra, xcd = nx >> 3, nx & 7, bx & 7
+        return xcd * per + min(xcd, extra) + (bx >> 3)
+
+    # main launch: items [0, N - tail), whole key ranges, rows written to O directly
+    n_main = N - tail
+    lids = sorted(xcd_lid(bx, n_main) for bx in range(n_main))
+    assert lids == list(range(n_main))
+    for item in range(n_main):
+        b, kvh, rh, rpos, rok, L, n_tiles = item_rows(item)
+        np.add.at(owned, (b, rh[rok], rpos[rok]), 1)
+    # split launch
+    nx = tail * parts
+    seen = set()
+    for bx in range(nx):
+        lid = xcd_lid(bx, nx)
+        assert 0 <= lid < nx and lid not in seen
+        seen.add(lid)
+        item, part = n_main + lid // parts, lid % parts
+        assert n_main <= item < N
+        b, kvh, rh, rpos, rok, L, n_tiles = item_rows(item)
+        tp = -(-n_tiles // parts) if n_tiles else 0
+        j0 = min(part * tp, n_tiles)
+        j1 = min(n_tiles, j0 + tp)
+        assert 0 <= j0 <= j1 <= n_tiles
+        copy_tiles(b, kvh, L, j0, j1)
+        prow = (lid // parts) * R + rows_w
+        assert prow.min() >= 0 and prow.max() < rows
+        slot = prow * parts + part
+        assert slot.max() < part_lse_elems and (slot.max() + 1) * D <= part_o_elems
+        if part == 0:
+            off = b * q_sb + rh * q_sh + rpos * q_ss
+            assert (row_map[prow] == -2).all(), "a row-map entry written twice"
+            row_map[prow] = np.where(rok, off, -1)
+            assert off[rok].size == 0 or (off[rok].min() >= 0 and off[rok].max() + D <= o_elems)
+            np.add.at(owned, (b, rh[rok], rpos[rok]), 1)
+    assert (row_map != -2).all(), "a row-map entry never written"
+    # combine: pair i reads slots i * parts + s, s < parts, and writes row_map[i] (if >= 0)
+    pairs = np.arange(rows)
+    assert ((pairs * parts + parts - 1) < part_lse_elems).all()
+    assert ((pairs * parts + parts) * D <= part_o_elems).all()
+    assert (owned == 1).all(), "a query row is owned by no launch or by several"
+
+
+TAIL_CASES = [
+    # (D, B, Hq, Hkv, Sq, Sk, tail, parts, paged, lens)
+    (128, 1, 4, 4, 1024, 4096, 32, 8, False, None),          # every item split (first round)
+    (128, 2, 8, 2, 300, 900, 20, 4, True, (900, 640)),       # the graph-test shape
+    (64, 2, 8, 2, 200, 700, 8, 5, True, (700, 0)),           # a sequence with no key
+    (128, 1, 16, 2, 90, 150, 1, 64, True, None),             # 64 parts of 3 tiles
+    (256, 2, 4, 2, 130, 500, 6, 5, True, (500, 64)),         # narrow d = 256 form
+    (128, 1, 17, 17, 16384, 256, 64, 4, False, None),        # eight-wave form, quarter-full round
+    (256, 1, 5, 5, 8192, 512, 64, 4, False, None),           # narrow form, 320 items
+]
+
+
+@pytest.mark.parametrize("case", TAIL_CASES, ids=lambda c: f"d{c[0]}_B{c[1]}_{c[2]}x{c[3]}_{c[4]}x{c[5]}_t{c[6]}p{c[7]}")
+def test_tail_split_addresses_in_bounds(case):
+    D, B, Hq, Hkv, Sq, Sk, tail, parts, paged, lens = case
+    check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged, lens)
 
 
 def test_long_workload_launch_form_and_offsets():
