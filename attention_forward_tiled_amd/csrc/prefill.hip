@@ -832,6 +832,7 @@ hipError_t launch_ng(const PrefillParams& p, int64_t blocks, hipStream_t stream)
 struct Form {
   int nw = 4, ng = 1;
   bool pair = false, narrow = false;
+  bool fill = false;      // a causal two-group launch that leaves at least half of the CUs idle
   int bq = 0;
   int64_t blocks = 0;     // workgroups of the launch
   int64_t items = 0;      // work items (query blocks of one (sequence, KV head))
@@ -870,6 +871,10 @@ Form choose_form(const PrefillParams& p) {
       if (nq > 1 && f.blocks >= 2 * (int64_t)std::max(p.cus, 1)) {
         f.pair = true;
         f.blocks = (nq + 1) / 2 * p.hkv * p.batch;
+      } else if (2 * f.blocks <= (int64_t)std::max(p.cus, 1)) {
+        // few items: their key ranges may instead be split over four-wave workgroups
+        // (plan_one decides; launch_one keeps the two-group form if it does not split)
+        f.fill = true;
       }
     }
   }
@@ -901,14 +906,19 @@ hipError_t resident_per_cu(int* n) {
   return hipSuccess;
 }
 
-// Tail split: only for launches whose items all have the same key range (non-causal, one
+// Tail split: for launches whose items all have the same key range (non-causal, one
 // group); the split pays once the items are long enough that the partial writes and the
 // combine cost less than the idle CUs of the last round. The library splits when the
 // tail items would leave at least half of the CUs without work: with several resident
 // workgroups per CU, a last round that still reaches every CU is not slower in proportion
 // to its empty slots (fewer workgroups share each CU), and splitting it did not pay
 // (d = 64, a half-full round of three workgroups per CU: +1.6% time).
+// Causal launches with few items (their two-group workgroups would leave at least half of
+// the CUs idle, as chunked prefill of a few short chunks does) split every item instead,
+// over four-wave workgroups, when the keys reach kFillMinTiles tiles: 18-42% faster on
+// such shapes, slower with 1024-2048 keys, where the partial writes dominate.
 constexpr int kTailMinTiles = 32;     // keys per item >= 2048 when the library chooses
+constexpr int kFillMinTiles = 48;     // causal few-item launches: keys >= 3072
 constexpr int kTailMaxParts = 16;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -923,18 +933,22 @@ hipError_t plan_one(const PrefillParams& p, int kv_splits, PrefillPlan* plan) {
     return hipSuccess;
   } else {
     const int n_tiles = (p.seqlen_k + kPage - 1) / kPage;
-    if (kv_splits == 1 || p.causal || f.ng != 1 || n_tiles == 0) return hipSuccess;
+    const bool fill = f.fill && D <= 128;   // causal few items: every item, one-group form
+    if (kv_splits == 1 || n_tiles == 0 || !(fill || (!p.causal && f.ng == 1))) return hipSuccess;
     int occ = 1;
     hipError_t e;
     if constexpr (D == 256) e = resident_per_cu<D, 0, T>(&occ);
-    else e = f.nw == 8 ? resident_per_cu<D, 8, T>(&occ) : resident_per_cu<D, 4, T>(&occ);
+    else e = (f.nw == 8 && !fill) ? resident_per_cu<D, 8, T>(&occ) : resident_per_cu<D, 4, T>(&occ);
     if (e != hipSuccess) return e;
     const int64_t cap = (int64_t)occ * std::max(p.cus, 1);
-    const int64_t tail = f.items % cap;
+    const int64_t tail = fill ? f.items : f.items % cap;
     if (tail == 0) return hipSuccess;
     int64_t parts;
     if (kv_splits >= 2) {
       parts = kv_splits;
+    } else if (fill) {
+      if (n_tiles < kFillMinTiles) return hipSuccess;
+      parts = std::min<int64_t>({std::max<int64_t>(cap / tail, 2), kTailMaxParts, n_tiles / 8});
     } else {
       if (2 * tail > std::max(p.cus, 1) || n_tiles < kTailMinTiles) return hipSuccess;
       parts = std::min<int64_t>({cap / tail, kTailMaxParts, n_tiles / 8});
@@ -973,7 +987,7 @@ hipError_t launch_one(const PrefillParams& p0, const PrefillPlan& plan, hipStrea
     }
   };
   if constexpr (D <= 128) {
-    if (f.ng == 2) {
+    if (f.ng == 2 && !(f.fill && plan.parts >= 2)) {
       return f.pair ? launch_ng<D, 2, 4, T, PRECISE, true>(p, f.blocks, stream)
                     : launch_ng<D, 2, 4, T, PRECISE>(p, f.blocks, stream);
     }

@@ -119,17 +119,20 @@ typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
  * sequence and KV head); when the last round of items on the device's CUs would leave
  * CUs idle, the library can give the key tiles of each of those last items to several
  * workgroups, which write fp32 partial outputs into the workspace, and merge the
- * partials afterwards exactly as attn_splitkv_combine does. This is done only for
+ * partials afterwards exactly as attn_splitkv_combine does. This is done for
  * non-causal launches with precise = 0 (the items of such a launch all have the same
- * key range). A split row's O is the same attention up to fp32 rounding
+ * key range), and for causal launches with precise = 0 and d <= 128 whose items are so
+ * few that at most half of the CUs would have one: then every item is split (chunked
+ * prefill of a few short chunks against long keys). A split row's O is the same attention up to fp32 rounding
  * and the fp16/bf16 rounding of P against a different running maximum: within the
  * tolerances of the unsplit result, not bit-identical to it.
  *  kv_splits  0: the library splits when the items of the last round would leave at
- *             least half of the CUs idle and the items have at least 2048 keys (up to
- *             16 parts); 1: never split;
- *             2..ATTN_MAX_SPLITS: split the tail items into that many parts whenever
- *             the last round is not full (every item when the launch has fewer items
- *             than one round).
+ *             least half of the CUs idle and the items have at least 2048 keys (3072
+ *             for the causal case; up to 16 parts); 1: never split;
+ *             2..ATTN_MAX_SPLITS: split into that many parts whenever the launch
+ *             qualifies (non-causal: the last round is not full, and every item is in
+ *             it when the launch has fewer items than one round; causal: few items as
+ *             above).
  *  workspace, workspace_bytes  device scratch for the partials, 256-byte aligned, at
  *             least attn_prefill_workspace_bytes(args) bytes; caller-owned and only
  *             used in stream order by this call, so calls that may overlap need

@@ -228,7 +228,7 @@ def test_prefill_packed_query_addresses_in_bounds():
     check_prefill(64, 3, 4, 4, 200, 130, False, False, lens=(130, 7, 130), cu=np.array([0, 33, 233, 234]))
 
 
-def check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged=False, lens=None):
+def check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged=False, lens=None, causal=False):
     """The tail split of a non-causal one-group launch (plan_one / launch_one and the
     split mode of both prefill kernels): the main launch takes items [0, N - tail), the
     split launch's unit u (through the same XCD permutation) takes part u % parts of item
@@ -237,7 +237,12 @@ def check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged=False, lens=None)
     launches own every query row exactly once; the combine reads only inside the
     partials."""
     G = Hq // Hkv
-    NG, NW, PAIR, bq = prefill_form(D, False, G, Sq, Sk, B, Hkv)
+    NG, NW, PAIR, bq = prefill_form(D, causal, G, Sq, Sk, B, Hkv)
+    if causal:
+        # a causal launch splits only in place of a two-group launch of few items, and
+        # then runs the one-group four-wave form over every item
+        assert NG == 2 and not PAIR and tail == -(-Sq // bq) * Hkv * B
+        NG, NW = 1, 4
     assert NG == 1 and not PAIR
     R = 16 * 8 if D == 256 else 32 * NW            # rows per item (narrow: 8 waves x 16)
     assert R == NW * 32                            # the same rows as the four-wave model
@@ -270,7 +275,9 @@ def check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged=False, lens=None)
         rh = kvh * G + hig
         rok = (hig < G) & (rpos < Sq)
         L = min(max(int(lens[b]), 0), Sk)
-        n_tiles = (L + PAGE - 1) // PAGE if (L > 0 and q0 < Sq) else 0
+        pmax = min(q0 + bq, Sq) - 1
+        kv_end = min(L, pmax + (L - Sq) + 1) if causal else L
+        n_tiles = (kv_end + PAGE - 1) // PAGE if (kv_end > 0 and q0 < Sq) else 0
         return b, kvh, rh, rpos, rok, L, n_tiles
 
     def copy_tiles(b, kvh, L, j0, j1):
@@ -340,12 +347,25 @@ TAIL_CASES = [
     (128, 1, 17, 17, 16384, 256, 64, 4, False, None),        # eight-wave form, quarter-full round
     (256, 1, 5, 5, 8192, 512, 64, 4, False, None),           # narrow form, 320 items
 ]
+CAUSAL_TAIL_CASES = [
+    # causal launches with few items: every item split, four-wave one-group form
+    (128, 2, 16, 4, 256, 4096, 64, 8, True, (4096, 3000)),   # chunked prefill, ragged keys
+    (128, 2, 8, 2, 200, 700, 28, 3, True, (700, 300)),
+    (64, 1, 4, 4, 300, 300, 12, 4, False, None),              # self-attention, empty parts
+    (128, 2, 16, 4, 90, 60, 24, 2, True, (60, 0)),           # keys shorter than queries
+]
 
 
 @pytest.mark.parametrize("case", TAIL_CASES, ids=lambda c: f"d{c[0]}_B{c[1]}_{c[2]}x{c[3]}_{c[4]}x{c[5]}_t{c[6]}p{c[7]}")
 def test_tail_split_addresses_in_bounds(case):
     D, B, Hq, Hkv, Sq, Sk, tail, parts, paged, lens = case
     check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged, lens)
+
+
+@pytest.mark.parametrize("case", CAUSAL_TAIL_CASES, ids=lambda c: f"d{c[0]}_B{c[1]}_{c[2]}x{c[3]}_{c[4]}x{c[5]}_p{c[7]}")
+def test_causal_split_addresses_in_bounds(case):
+    D, B, Hq, Hkv, Sq, Sk, tail, parts, paged, lens = case
+    check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged, lens, causal=True)
 
 
 def test_long_workload_launch_form_and_offsets():

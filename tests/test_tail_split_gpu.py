@@ -4,7 +4,7 @@ unified attention, from the math up", section 8; the 7minutos.es article on Moon
 AI's HIP attention kernel, paragraph "Punto de referencia"). Forced part counts on small
 shapes (every item is then in the tail) against the fp64 oracle, O and lse; the
 library's own choice on shapes whose last round is partly empty, in the four-wave, the
-eight-wave and the d = 256 narrow forms."""
+eight-wave and the d = 256 narrow forms, and on a causal launch with few items."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +31,13 @@ FORCED = [
     (P("split_bf16_d256_dense_ragged", 2, 2, 2, 200, 700, 256, "bf16", False, "dense"), 3),
     (P("split_f16_d256_gqa2_paged_varlen_f32out", 2, 4, 2, 130, 500, 256, "f16", False, "paged",
        seqlens_k=(500, 64), out_dtype="f32"), 5),
+    # causal launches with few items: every item split (bottom-right mask per part,
+    # diagonal tiles in any part, rows whose keys all fall in other parts)
+    (P("split_f16_d128_causal_chunk_paged", 2, 8, 2, 200, 700, 128, "f16", True, "paged",
+       seqlens_k=(700, 300)), 3),
+    (P("split_bf16_d64_causal_self_dense", 1, 4, 4, 300, 300, 64, "bf16", True, "dense"), 4),
+    (P("split_bf16_d128_causal_gqa4_short_keys", 2, 16, 4, 90, 60, 128, "bf16", True, "paged",
+       seqlens_k=(60, 0)), 2),
 ]
 
 
@@ -118,7 +125,7 @@ def _sampled_check(case, inp, O, rows_of):
             K = bits_to_f64(inp_k[b, :, h // G, :], case.dtype)
             V = bits_to_f64(inp_v[b, :, h // G, :], case.dtype)
             Oref, _ = oracle.attention_rows(bits_to_f64(inp_q[b, rows, h, :], case.dtype), K, V, rows,
-                                            case.seqlen_k, case.seqlen_q, False, 1.0 / np.sqrt(d))
+                                            case.seqlen_k, case.seqlen_q, case.causal, 1.0 / np.sqrt(d))
             worst = max(worst, max_abs_err(O[b, rows, h, :], Oref))
     return worst
 
@@ -131,6 +138,8 @@ AUTO = [
     P("auto_f16_d128_h17_s16384x2048_wg8", 1, 17, 17, 16384, 2048, 128, "f16", False, "dense", poison=False),
     # d = 256 narrow kernel: 5 heads x 64 query blocks = 320 items, the last 64 split
     P("auto_bf16_d256_h5_s8192x4096", 1, 5, 5, 8192, 4096, 256, "bf16", False, "dense", poison=False),
+    # causal chunked prefill with few items: 2 x 4 KV heads x 8 blocks = 64 items, each split
+    P("auto_bf16_d128_causal_chunk_256x4096", 2, 16, 4, 256, 4096, 128, "bf16", True, "dense", poison=False),
 ]
 
 
