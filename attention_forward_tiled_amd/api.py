@@ -75,7 +75,7 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
 
     Tail split (precise off): ``kv_splits`` 0 lets the library split the key range of
     the last round of work items when that round would leave half of the CUs idle
-    (non-causal), or of every item when a causal launch has that few items (d <= 128);
+    (non-causal), or of every item when a causal launch has that few items;
     1 turns it off, n >= 2 splits those items into n parts. The partials go to ``workspace``
     (uint8 device tensor of at least attn_prefill_workspace_bytes bytes), allocated here
     when the call needs one and none is given.

@@ -861,6 +861,7 @@ Form choose_form(const PrefillParams& p) {
   if constexpr (D == 256 && !PRECISE) {
     // d = 256: eight waves of 16 rows (two per SIMD) in place of four of 32 (one per SIMD)
     f.narrow = true; f.nw = 8;
+    f.fill = p.causal && 2 * f.blocks <= (int64_t)std::max(p.cus, 1);
     return f;
   }
   if constexpr (D <= 128) {
@@ -933,7 +934,7 @@ hipError_t plan_one(const PrefillParams& p, int kv_splits, PrefillPlan* plan) {
     return hipSuccess;
   } else {
     const int n_tiles = (p.seqlen_k + kPage - 1) / kPage;
-    const bool fill = f.fill && D <= 128;   // causal few items: every item, one-group form
+    const bool fill = f.fill;   // causal few items: every item (one-group or narrow form)
     if (kv_splits == 1 || n_tiles == 0 || !(fill || (!p.causal && f.ng == 1))) return hipSuccess;
     int occ = 1;
     hipError_t e;

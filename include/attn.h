@@ -121,9 +121,9 @@ typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
  * workgroups, which write fp32 partial outputs into the workspace, and merge the
  * partials afterwards exactly as attn_splitkv_combine does. This is done for
  * non-causal launches with precise = 0 (the items of such a launch all have the same
- * key range), and for causal launches with precise = 0 and d <= 128 whose items are so
- * few that at most half of the CUs would have one: then every item is split (chunked
- * prefill of a few short chunks against long keys). A split row's O is the same attention up to fp32 rounding
+ * key range), and for causal launches with precise = 0 whose items are so few that at
+ * most half of the CUs would have one: then every item is split (chunked prefill of a
+ * few short chunks against long keys). A split row's O is the same attention up to fp32 rounding
  * and the fp16/bf16 rounding of P against a different running maximum: within the
  * tolerances of the unsplit result, not bit-identical to it.
  *  kv_splits  0: the library splits when the items of the last round would leave at

@@ -239,9 +239,10 @@ def check_tail_split(D, B, Hq, Hkv, Sq, Sk, tail, parts, paged=False, lens=None,
     G = Hq // Hkv
     NG, NW, PAIR, bq = prefill_form(D, causal, G, Sq, Sk, B, Hkv)
     if causal:
-        # a causal launch splits only in place of a two-group launch of few items, and
-        # then runs the one-group four-wave form over every item
-        assert NG == 2 and not PAIR and tail == -(-Sq // bq) * Hkv * B
+        # a causal launch splits only when it has few items, every one of them: in place
+        # of a two-group launch (then in the one-group four-wave form), or at d = 256
+        assert tail == -(-Sq // bq) * Hkv * B and not PAIR
+        assert NG == 2 or D == 256
         NG, NW = 1, 4
     assert NG == 1 and not PAIR
     R = 16 * 8 if D == 256 else 32 * NW            # rows per item (narrow: 8 waves x 16)
@@ -353,6 +354,8 @@ CAUSAL_TAIL_CASES = [
     (128, 2, 8, 2, 200, 700, 28, 3, True, (700, 300)),
     (64, 1, 4, 4, 300, 300, 12, 4, False, None),              # self-attention, empty parts
     (128, 2, 16, 4, 90, 60, 24, 2, True, (60, 0)),           # keys shorter than queries
+    (256, 2, 4, 2, 150, 600, 12, 3, True, (600, 200)),       # narrow d = 256 form
+    (256, 1, 16, 4, 512, 8192, 64, 4, False, None),
 ]
 
 

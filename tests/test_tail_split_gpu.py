@@ -38,6 +38,8 @@ FORCED = [
     (P("split_bf16_d64_causal_self_dense", 1, 4, 4, 300, 300, 64, "bf16", True, "dense"), 4),
     (P("split_bf16_d128_causal_gqa4_short_keys", 2, 16, 4, 90, 60, 128, "bf16", True, "paged",
        seqlens_k=(60, 0)), 2),
+    (P("split_f16_d256_causal_chunk_gqa2", 2, 4, 2, 150, 600, 256, "f16", True, "paged",
+       seqlens_k=(600, 200)), 3),
 ]
 
 
@@ -140,6 +142,7 @@ AUTO = [
     P("auto_bf16_d256_h5_s8192x4096", 1, 5, 5, 8192, 4096, 256, "bf16", False, "dense", poison=False),
     # causal chunked prefill with few items: 2 x 4 KV heads x 8 blocks = 64 items, each split
     P("auto_bf16_d128_causal_chunk_256x4096", 2, 16, 4, 256, 4096, 128, "bf16", True, "dense", poison=False),
+    P("auto_bf16_d256_causal_chunk_512x8192", 1, 16, 4, 512, 8192, 256, "bf16", True, "dense", poison=False),
 ]
 
 
