@@ -123,6 +123,11 @@ CONFIGS = {
         seqlen_k=4096, head_dim=64, dtype="f16", causal=True, kv="dense", layout="bshd",
         poison=False),
     # Long non-causal MHA self-attention, dense BSHD K/V, inputs 0.5*N(0,1).
+    # Chunked prefill of two short chunks: 2 x 4 KV heads x 8 query blocks = 64 items,
+    # too few for the CUs (the causal few-item split).
+    "chunked_small_bf16_2x256x4096": PrefillCase(
+        "chunked_small_bf16_2x256x4096", batch=2, heads_q=16, heads_kv=4, seqlen_q=256,
+        seqlen_k=4096, head_dim=128, dtype="bf16", causal=True, kv="paged", table="random"),
     # A launch whose last round of work items is a quarter full (25 heads x 64 query
     # blocks of 256 rows on 256 CUs): the shape of the prefill tail split.
     "tail_noncausal_bf16_h25_s16384": PrefillCase(
