@@ -43,6 +43,7 @@
 //   * The workgroup order is reversed over query blocks so that, under a causal
 //     mask, the longest-running blocks are dispatched first.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -887,9 +888,9 @@ Form choose_form(const PrefillParams& p) {
 // narrow d = 256 kernel.
 template <int D, int NW, typename T>
 hipError_t resident_per_cu(int* n) {
-  static int cached = 0;
-  if (cached > 0) {
-    *n = cached;
+  static std::atomic<int> cached{0};   // the same for every gfx950 device; callers may race
+  if (const int c = cached.load(std::memory_order_relaxed); c > 0) {
+    *n = c;
     return hipSuccess;
   }
   int v = 0;
@@ -902,8 +903,9 @@ hipError_t resident_per_cu(int* n) {
         &v, reinterpret_cast<const void*>(&prefill_kernel<D, 1, NW, T, false, false>), 64 * NW, 0);
   }
   if (e != hipSuccess) return e;
-  cached = std::max(v, 1);
-  *n = cached;
+  v = std::max(v, 1);
+  cached.store(v, std::memory_order_relaxed);
+  *n = v;
   return hipSuccess;
 }
 
