@@ -223,9 +223,9 @@ attn_status_t decode_impl(const attn_decode_args_t* a, void* stream, bool noallo
     const int64_t rmax = ((int64_t)a->max_seqlen_k + ATTN_PAGE_SIZE - 1) / ATTN_PAGE_SIZE;
     const int cus = device_cus();
     if (a->num_splits >= 2 && (int64_t)a->batch * rmax < (int64_t(1) << 30) && cus > 0) {
-      // persistent workgroups per KV head: one per CU (two at d = 64, whose ring is half
-      // the LDS)
-      const int per_cu = a->head_dim == 64 ? 2 : 1;
+      // persistent workgroups per KV head: two per CU at d <= 128 (their rings take half
+      // the LDS each), one at d = 256
+      const int per_cu = a->head_dim <= 128 ? 2 : 1;
       p.nwk = std::max(1, std::min(kMaxStreamWG, per_cu * cus / a->num_heads_kv));
       c.seqlens_k = a->seqlens_k; c.heads = a->num_heads_q; c.max_seqlen_k = a->max_seqlen_k;
       if (attn_status_t st = launch_status(attn::launch_decode_stream(p, a->head_dim, a->qkv_dtype, s),

@@ -18,7 +18,7 @@
 //     byte is read once.
 //   * Pages stream through a ring of LDS stages (K tile and V tile of one 64-key page
 //     per stage) filled by global_load_lds_dwordx4, which needs no registers for the
-//     data in flight; the ring is several pages deep, and page i + NST - 1 is started
+//     data in flight; the ring is two to four pages deep, and page i + NST - 1 is started
 //     as soon as page i is published, so up to NST - 1 pages are in flight while page
 //     i is consumed. The K/V copies are non-temporal: every page is read once, and
 //     marking the stream so keeps it from displacing reusable cache lines (12% faster).
@@ -346,11 +346,12 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
   }
 }
 
-// Ring depth of the stream kernel: 144 KiB of stages (K tile, V tile, Q block) per
-// workgroup at d = 128 and 256, one workgroup per CU. At d = 64 (two pages consumed per
-// barrier) 80 KiB, so that two workgroups share a CU: a second wave per SIMD hides part
-// of the per-page chain of dependent steps (+2% against eight stages and one workgroup).
-template <int D> constexpr int kStreamStages = D == 64 ? 4 : (D == 128 ? 4 : 2);
+// Ring depth of the stream kernel, in stages of (K tile, V tile, Q block): at d = 64
+// (two pages consumed per barrier) four stages, 80 KiB, and at d = 128 two, 72 KiB, so
+// that two workgroups share a CU: a second wave per SIMD hides part of the per-page chain
+// of dependent steps (+2% each against one workgroup with all the LDS, eight and four
+// stages). At d = 256 two stages of 72 KiB, one workgroup per CU.
+template <int D> constexpr int kStreamStages = D == 64 ? 4 : 2;
 
 // Balanced (persistent) split kernel. Workgroup w serves KV head w % Hkv and unit range
 // j = w / Hkv of the plan; the workgroups of the Hkv heads with the same j walk the
