@@ -82,8 +82,9 @@ def test_paged_equals_dense_bitwise():
 
 
 @pytest.mark.parametrize("name", ["tiny_causal_f16_d64", "gqa_causal_paged_f16_s2048",
-                                  "chunked_prefill_bf16_512x4096"])
+                                  "chunked_prefill_bf16_512x4096", "chunked_small_bf16_2x256x4096"])
 def test_named_prefill_full(name):
+    # (the last runs the causal few-item split: 64 items over 8 key parts and the combine)
     case = CONFIGS[name]
     say(f"prefill parity (full output) {name}")
     inp = make_prefill_inputs(case, seed=0)
@@ -120,10 +121,11 @@ def _every_wave_check(case, seed=0):
 
 
 @pytest.mark.parametrize("name", ["long_noncausal_bf16_s16384", "causal_mha_bf16_d256_s4096",
-                                  "causal_mha_f16_d64_s4096"])
+                                  "causal_mha_f16_d64_s4096", "tail_noncausal_bf16_h25_s16384"])
 def test_named_full_size_every_wave(name):
     # the long workload in the eight-wave form (4096 workgroups of 256 rows, 32768 rows
-    # checked), and the d = 256 and d = 64 causal workloads in their four-wave forms
+    # checked), the d = 256 and d = 64 causal workloads in their launch forms, and the
+    # 25-head workload with its tail split (1536 items, then 64 items in 4 key parts)
     case = CONFIGS[name]
     say(f"prefill parity (one row per wave of every workgroup) {name}")
     _every_wave_check(case)
