@@ -163,3 +163,34 @@ def test_tail_split_library_choice(case):
         np.arange(0, S, 32) + rng.integers(0, 32, -(-S // 32)), S - 1))
     say(f"  max abs err {worst:.3e} (tol {tolerance(case)})")
     assert worst <= tolerance(case)
+
+
+POLICY = [
+    # (case, splits?) for the library's own choice (kv_splits = 0) on 256 CUs
+    (P("long_noncausal_bf16_s16384", 4, 16, 16, 16384, 16384, 128, "bf16", False, "dense"), False),  # 16 full rounds
+    (P("gqa_causal_paged_f16_s2048", 1, 32, 8, 2048, 2048, 128, "f16", True, "paged"), False),      # paired form
+    (P("chunked_prefill_bf16_512x4096", 4, 16, 4, 512, 4096, 128, "bf16", True, "paged"), False),   # one item per CU
+    (P("causal_mha_bf16_d256_s4096", 2, 16, 16, 4096, 4096, 256, "bf16", True, "dense"), False),
+    (P("tail_noncausal_bf16_h25_s16384", 1, 25, 25, 16384, 16384, 128, "bf16", False, "dense"), True),
+    (P("chunked_small_bf16_2x256x4096", 2, 16, 4, 256, 4096, 128, "bf16", True, "paged"), True),
+    (P("half_full_d64_round", 3, 6, 6, 8192, 8192, 64, "bf16", False, "dense"), False),  # every CU still busy
+    (P("short_causal_chunks_2048", 1, 32, 8, 512, 2048, 128, "f16", True, "paged"), False),  # keys < 3072
+    (P("short_noncausal_1024", 1, 4, 4, 1024, 1024, 128, "bf16", False, "dense"), False),   # keys < 2048
+    (P("precise_noncausal", 1, 4, 4, 1024, 4096, 128, "f16", False, "dense", precise=True, out_dtype="f32"), False),
+]
+
+
+@pytest.mark.parametrize("case,splits", POLICY, ids=lambda x: getattr(x, "name", str(x)))
+def test_tail_split_policy(case, splits):
+    """Which launches the library splits by itself (the rule of the split planner)."""
+    from attention_forward_tiled_amd import attn_device_info
+    if attn_device_info(0)["compute_units"] != 256:
+        pytest.skip("the rule is stated for 256 CUs")
+    say(f"tail split policy {case.name}: expect {'split' if splits else 'no split'}")
+    from attention_forward_tiled_amd import attn_prefill_workspace_bytes
+    shape = ((case.batch, case.seqlen_q, case.heads_q, case.head_dim) if case.layout == "bshd"
+             else (case.batch, case.heads_q, case.seqlen_q, case.head_dim))
+    q = torch.empty(shape, dtype={"f16": torch.float16, "bf16": torch.bfloat16}[case.dtype], device="cuda")
+    need = attn_prefill_workspace_bytes(q, num_heads_kv=case.heads_kv, seqlen_k=case.seqlen_k, causal=case.causal,
+                                        layout=case.layout, precise=case.precise)
+    assert (need > 0) == splits, need
