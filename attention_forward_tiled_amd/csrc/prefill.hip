@@ -233,7 +233,7 @@ void prefill_kernel(const PrefillParams p) {
   float16v acc[DB];
 
   // One tile from stage STAGE of this group: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto compute = [&](int j, auto stage_c, auto mask_c) {
+  auto compute = [&](int j, auto stage_c, auto mask_c, auto&& mid) {
     constexpr int STAGE = decltype(stage_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
     const char* ks = reinterpret_cast<const char*>(smem) + STAGE * 2 * TILE * 2;
@@ -250,6 +250,8 @@ void prefill_kernel(const PrefillParams p) {
         sc[kb] = Op<T>::mfma32(as_op<T>(a), as_op<T>(qf[s]), sc[kb]);
       }
     }
+
+    mid();   // (the two-group form's group 1 issues its next tile here)
 
     if constexpr (MASK) {
 #pragma unroll
@@ -353,8 +355,15 @@ void prefill_kernel(const PrefillParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     const int j = j0 + i;
-    if (j + 1 < j1) issue_tile(j + 1, STAGE ^ 1);
-    if (((stage_ok >> STAGE) & 1u) && j < j1) compute(j, stage_c, mask_c);
+    // two-group form at d = 128: group 0 issues the next tile's copies now, group 1 after
+    // its S^T products, so that on each SIMD one wave issues copies while the other
+    // computes (+1 to +3% on the causal shapes of this form, bit-equal; at d = 64, with
+    // half the products per tile, -1%)
+    const bool late = NG == 2 && D == 128 && grp == 1;
+    if (j + 1 < j1 && !late) issue_tile(j + 1, STAGE ^ 1);
+    auto mid = [&]() { if (late && j + 1 < j1) issue_tile(j + 1, STAGE ^ 1); };
+    if (((stage_ok >> STAGE) & 1u) && j < j1) compute(j, stage_c, mask_c, mid);
+    else mid();
   };
 
   for (int it = 0; it < (PAIR ? 2 : 1); ++it) {

@@ -52,8 +52,9 @@ def _head_dim(name):
 def test_hot_kernels_fit_their_register_budgets(built):
     """Two waves per SIMD (eight-wave workgroups, or two four-wave workgroups per CU) need
     at most 256 registers (VGPR + AGPR) a lane; spills to scratch memory are confined to
-    the precise d = 256 path and the paired two-group form (2 registers, outside the
-    tile loop); every kernel fits the 160 KiB of LDS of a CU."""
+    the precise d = 256 path and the paired two-group form at d = 128 (a few registers,
+    stored before the tile loops and reloaded once per item); every kernel fits the
+    160 KiB of LDS of a CU."""
     pre = build.kernel_resources(build.device_asm("prefill.hip", built))
     dec = build.kernel_resources(build.device_asm("decode.hip", built))
     narrow = [k for k in pre if "prefill_narrow_kernel" in k]
@@ -68,7 +69,8 @@ def test_hot_kernels_fit_their_register_budgets(built):
         if d == 256:
             continue                     # precise d = 256: one wave per SIMD, 512 registers
         assert r["vgpr"] + r["agpr"] <= 256, (k, r)
-        assert r["vgpr_spill"] <= (2 if d == 128 else 0), (k, r)
+        paired = k.endswith("Lb1EEEvNS_13PrefillParamsE")
+        assert r["vgpr_spill"] <= (8 if d == 128 and paired else 0), (k, r)
     for k, r in dec.items():
         assert r["vgpr_spill"] == 0 and r["scratch"] == 0, (k, r)
     for k, r in {**pre, **dec}.items():
