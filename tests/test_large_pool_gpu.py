@@ -1,8 +1,11 @@
-"""Paged K/V caches larger than 4 GiB. The pages that the block table names lie past
-byte offset 2^32 of the pool and on both sides of 2^31, so the kernels' copy addresses
-carry a high word and low words with bit 31 set, through the wave-uniform base plus
-per-lane offset copies (prefill) and the per-lane address copies (decode, ragged
-tails). Every launch must match the fp64 oracle run on the same pages stored compactly."""
+"""K/V buffers larger than 4 GiB. The pages that a block table names lie past byte
+offset 2^32 of the pool and on both sides of 2^31 (and dense K/V put a sequence or heads
+past those offsets), so the kernels' copy addresses carry a high word and low words with
+bit 31 set, through the wave-uniform base plus per-lane offset copies (prefill) and the
+per-lane address copies (decode, ragged tails). Every launch must match the fp64 oracle
+run on the same keys stored compactly."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -130,5 +133,47 @@ def test_decode_pages_past_4gib(case):
         say(f"  max abs err {err:.3e}")
         assert err <= TOL[case.dtype]
         assert np.abs(to_f64(lse) - lref).max() <= lse_tolerance(case.dtype)
+    del k, v
+    torch.cuda.empty_cache()
+
+
+DENSE = [
+    # dense K/V of 2^20 keys per sequence (4 GiB per sequence and tensor): the second
+    # sequence starts past byte 2^32 (BSHD), or heads 8 and on start past 2^31 (BHSD);
+    # only the first keys of each sequence are used
+    (P("bf16_d128_gqa2_noncausal_dense_bshd_big", 2, 32, 16, 300, 1 << 20, 128, "bf16", False, "dense",
+       seqlens_k=(500, 700)), 700),
+    (P("f16_d128_gqa2_causal_dense_bhsd_big", 2, 32, 16, 300, 1 << 20, 128, "f16", True, "dense",
+       layout="bhsd", seqlens_k=(640, 333)), 640),
+]
+
+
+@pytest.mark.parametrize("case,used", DENSE, ids=lambda x: getattr(x, "name", str(x)))
+def test_prefill_dense_kv_past_4gib(case, used):
+    from attention_forward_tiled_amd import attn_prefill_fwd
+    small = dataclasses.replace(case, seqlen_k=used)
+    inp = make_prefill_inputs(small, seed=35)
+    bhsd = case.layout == "bhsd"
+    shape = (case.batch, case.heads_kv, case.seqlen_k, case.head_dim) if bhsd else \
+        (case.batch, case.seqlen_k, case.heads_kv, case.head_dim)
+    say(f"prefill, dense K/V of {2 * np.prod(shape) / GIB:.1f} GiB each {case}")
+    k = torch.empty(shape, dtype=TORCH_DT[case.dtype], device="cuda")
+    v = torch.empty(shape, dtype=TORCH_DT[case.dtype], device="cuda")
+    if bhsd:
+        k[:, :, :used], v[:, :, :used] = dev(inp.k, case.dtype), dev(inp.v, case.dtype)
+    else:
+        k[:, :used], v[:, :used] = dev(inp.k, case.dtype), dev(inp.v, case.dtype)
+    Oref, lref = oracle_prefill(inp)
+    q = dev(inp.q, case.dtype)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full((case.batch, case.heads_q, case.seqlen_q), float("nan"), device="cuda")
+    attn_prefill_fwd(q, k, v, causal=case.causal, seqlens_k=dev_i32(inp.seqlens_k), seqlen_k=case.seqlen_k,
+                     layout=case.layout, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    err = max_abs_err(to_f64(out), Oref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[case.dtype]
+    assert np.abs(to_f64(lse) - lref).max() <= lse_tolerance(case.dtype)
     del k, v
     torch.cuda.empty_cache()
