@@ -167,6 +167,38 @@ def test_prefill_paired_sampled(case):
     assert err <= tolerance(case)
 
 
+# GQA ratios up to the supported 128: a four-wave item then holds 128 / G positions (one
+# at G >= 65, with rows 96..127 unused at G = 96), an eight-wave one 256 / G, a narrow
+# d = 256 one 128 / G; with a forced tail split in the four-wave form.
+WIDE_GROUPS = [
+    (P("bf16_d128_gqa128_causal_paged_two_groups", 1, 128, 1, 50, 300, 128, "bf16", True, "paged"), 0),
+    (P("f16_d64_gqa96_noncausal_dense_wg4", 2, 192, 2, 40, 200, 64, "f16", False, "dense",
+       seqlens_k=(200, 77)), 0),
+    (P("bf16_d128_gqa64_noncausal_paged_split", 1, 128, 2, 33, 700, 128, "bf16", False, "paged"), 5),
+    (P("bf16_d256_gqa64_causal_dense_narrow", 1, 128, 2, 30, 100, 256, "bf16", True, "dense"), 0),
+    (P("f16_d128_gqa128_noncausal_paged_wg8", 1, 256, 2, 1024, 150, 128, "f16", False, "paged"), 0),
+]
+
+
+@pytest.mark.parametrize("case,splits", WIDE_GROUPS, ids=lambda x: getattr(x, "name", str(x)))
+def test_prefill_wide_groups(case, splits):
+    say(f"prefill parity {case} kv_splits={splits}")
+    inp = make_prefill_inputs(case, seed=9)
+    O, lse = gpu_prefill(inp, with_lse=True, kv_splits=splits)
+    rows = np.arange(case.seqlen_q)
+    if case.seqlen_q > 256:
+        rows = np.unique(np.concatenate([[0, 1, 2, 3, case.seqlen_q - 2, case.seqlen_q - 1],
+                                         np.random.default_rng(4).choice(case.seqlen_q, 26, replace=False)]))
+    Oref, lref = oracle_prefill(inp, q_index=rows)
+    O, lse = (O[:, :, rows], lse[:, :, rows]) if case.layout == "bhsd" else (O[:, rows], lse[:, :, rows])
+    err = max_abs_err(O, Oref)
+    say(f"  max abs err {err:.3e} over {rows.size} rows x all (b, h)")
+    assert err <= tolerance(case)
+    fin = np.isfinite(lref)
+    assert (np.isneginf(lse) == ~fin).all()
+    assert np.abs(lse[fin] - lref[fin]).max() <= lse_tolerance(case.dtype, case.precise)
+
+
 EIGHT_WAVE = [
     P("f16_d64_gqa2_causal_paged_1024wg8", 4, 64, 32, 1024, 1024, 64, "f16", True, "paged"),
     P("bf16_d128_noncausal_dense_1024wg8", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense",
