@@ -18,6 +18,7 @@ ATTN_BSHD, ATTN_BHSD = 0, 1
 ATTN_ROUND_RTNE, ATTN_ROUND_RTNA, ATTN_ROUND_RTZ = 0, 1, 2
 ATTN_PAGE_SIZE = 64
 ATTN_MAX_SPLITS = 64
+ATTN_MAX_SEQLEN = 1 << 30
 ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 ATTN_ABI_VERSION = 5
 

@@ -145,6 +145,8 @@ attn_status_t decode_impl(const attn_decode_args_t* a, void* stream, bool noallo
     if (a->num_splits < 1 || a->num_splits > ATTN_MAX_SPLITS)
       return fail(ATTN_ERR_INVALID_ARG, "num_splits must be in [1, %d]", ATTN_MAX_SPLITS);
     if (a->max_seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_k must be >= 0");
+    if (a->max_seqlen_k > ATTN_MAX_SEQLEN)
+      return fail(ATTN_ERR_UNSUPPORTED, "max_seqlen_k must be <= %d (got %d)", ATTN_MAX_SEQLEN, a->max_seqlen_k);
     if (a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
       return fail(ATTN_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be positive");
     if ((int64_t)a->max_blocks_per_seq * ATTN_PAGE_SIZE < a->max_seqlen_k)
@@ -319,6 +321,8 @@ attn_status_t prefill_setup(const attn_prefill_args_t* a, attn::PrefillParams* p
   const int G = a->num_heads_q / a->num_heads_kv;
   if (G > 128) return fail(ATTN_ERR_UNSUPPORTED, "GQA ratio %d above 128 is not supported", G);
   if (a->seqlen_k < 0) return fail(ATTN_ERR_INVALID_ARG, "seqlen_k must be >= 0");
+  if (a->seqlen_q > ATTN_MAX_SEQLEN || a->seqlen_k > ATTN_MAX_SEQLEN)
+    return fail(ATTN_ERR_UNSUPPORTED, "seqlen_q and seqlen_k must be <= %d", ATTN_MAX_SEQLEN);
   if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if (a->batch > kMaxGridYZ || a->num_heads_kv > kMaxGridYZ)
     return fail(ATTN_ERR_UNSUPPORTED, "batch and num_heads_kv must be <= %lld", (long long)kMaxGridYZ);

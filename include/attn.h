@@ -42,6 +42,7 @@ extern "C" {
 #define ATTN_ABI_VERSION 5
 #define ATTN_PAGE_SIZE 64      /* tokens per KV page (block_size); equal to the KV tile width */
 #define ATTN_MAX_SPLITS 64     /* upper bound of num_splits for the split-KV decode */
+#define ATTN_MAX_SEQLEN (1 << 30)  /* upper bound of seqlen_q, seqlen_k and max_seqlen_k */
 #define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)  /* scratch of attn_decode_fwd_noalloc: 32 MiB */
 
 typedef enum {
@@ -143,6 +144,8 @@ typedef enum { ATTN_BSHD = 0, ATTN_BHSD = 1 } attn_layout_t;
  * count that is not a multiple, a paged cache whose table cannot hold seqlen_k
  * keys (64*max_blocks_per_seq < seqlen_k), bad enum values, packed queries with the
  * BHSD layout or a misaligned cu_seqlens_q, kv_splits outside [0, ATTN_MAX_SPLITS],
+ * seqlen_q or seqlen_k above ATTN_MAX_SEQLEN (UNSUPPORTED: positions are 32-bit in the
+ * kernels),
  * a split (kv_splits >= 2) without a workspace, or a workspace that is misaligned or
  * smaller than attn_prefill_workspace_bytes(args).
  */
@@ -204,13 +207,15 @@ size_t attn_prefill_workspace_bytes(const attn_prefill_args_t* args);
  *  q          [B, Hq, d] (the BSHD and BHSD layouts coincide at S_q = 1), qkv_dtype.
  *  k_cache, v_cache  [num_blocks, 64, Hkv, d], qkv_dtype.
  *  block_table int32 [B, max_blocks_per_seq]; seqlens_k int32 [B] (clamped to
- *             max_seqlen_k, which must be <= 64*max_blocks_per_seq).
+ *             max_seqlen_k, which must be <= 64*max_blocks_per_seq and
+ *             <= ATTN_MAX_SEQLEN).
  *  o          [B, Hq, d], o_dtype. lse: optional fp32 [B, Hq].
  *  workspace  device buffer of at least attn_decode_workspace_bytes(B, Hq,
  *             num_splits, d) bytes, 256-byte aligned; caller-owned scratch, reused
  *             freely between calls on the same stream.
  *  num_splits 1..ATTN_MAX_SPLITS. num_heads_q / num_heads_kv <= 16.
- * Errors: as for prefill, plus INVALID_ARG for a too-small or misaligned workspace.
+ * Errors: as for prefill (max_seqlen_k above ATTN_MAX_SEQLEN: UNSUPPORTED), plus
+ * INVALID_ARG for a too-small or misaligned workspace.
  */
 typedef struct {
   const void* q;

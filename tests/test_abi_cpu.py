@@ -36,6 +36,7 @@ def test_header_constants_match_binding():
     text = open(os.path.join(ROOT, "include", "attn.h")).read()
     assert f"#define ATTN_PAGE_SIZE {_lib.ATTN_PAGE_SIZE} " in text
     assert f"#define ATTN_MAX_SPLITS {_lib.ATTN_MAX_SPLITS} " in text
+    assert f"#define ATTN_MAX_SEQLEN (1 << {_lib.ATTN_MAX_SEQLEN.bit_length() - 1})" in text
     assert f"#define ATTN_ABI_VERSION {_lib.ATTN_ABI_VERSION}" in text
     assert f"#define ATTN_NOALLOC_SCRATCH_BYTES ({_lib.ATTN_NOALLOC_SCRATCH_BYTES >> 20}u << 20)" in text
 
@@ -93,6 +94,9 @@ BAD_PREFILL = [
     (dict(scale=float("nan")), _lib.ATTN_ERR_INVALID_ARG, "scale"),
     (dict(num_heads_q=258, num_heads_kv=2), _lib.ATTN_ERR_UNSUPPORTED, "GQA"),
     (dict(batch=-1), _lib.ATTN_ERR_INVALID_ARG, "batch"),
+    (dict(seqlen_q=(1 << 30) + 1), _lib.ATTN_ERR_UNSUPPORTED, "seqlen_q and seqlen_k must be <="),
+    (dict(seqlen_k=(1 << 30) + 1, max_blocks_per_seq=(1 << 24) + 1), _lib.ATTN_ERR_UNSUPPORTED,
+     "seqlen_q and seqlen_k must be <="),
     (dict(o_round=3), _lib.ATTN_ERR_INVALID_ARG, "o_round"),
     (dict(o_round=_lib.ATTN_ROUND_RTZ), _lib.ATTN_ERR_UNSUPPORTED, "fp16"),     # fp16 output
     (dict(cu_seqlens_q=FAKE, layout=_lib.ATTN_BHSD), _lib.ATTN_ERR_INVALID_ARG, "BSHD"),
@@ -152,6 +156,8 @@ BAD_DECODE = [
     (dict(workspace_bytes=16), _lib.ATTN_ERR_INVALID_ARG, "workspace"),
     (dict(workspace=FAKE + 16), _lib.ATTN_ERR_INVALID_ARG, "256-byte"),
     (dict(max_seqlen_k=321), _lib.ATTN_ERR_INVALID_ARG, "fewer than max_seqlen_k"),
+    (dict(max_seqlen_k=(1 << 30) + 1, max_blocks_per_seq=(1 << 24) + 1), _lib.ATTN_ERR_UNSUPPORTED,
+     "max_seqlen_k must be <="),
     (dict(block_table=None), _lib.ATTN_ERR_INVALID_ARG, "non-NULL"),
     (dict(head_dim=32), _lib.ATTN_ERR_INVALID_ARG, "head_dim"),
     (dict(qkv_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_INVALID_ARG, "qkv_dtype"),
