@@ -42,6 +42,13 @@
 //     the P.V MFMA consumes).
 //   * The workgroup order is reversed over query blocks so that, under a causal
 //     mask, the longest-running blocks are dispatched first.
+//   * d = 256 runs prefill_narrow_kernel instead: eight waves of 16 rows, two per SIMD
+//     (32 rows of d = 256 would need about 500 registers, one wave per SIMD).
+//   * Tail split (host: plan_one): when the last round of a non-causal launch, or a whole
+//     causal launch of few items, would leave at least half of the CUs idle, the key
+//     tiles of those items are cut into parts, one one-group workgroup per (item, part);
+//     each part writes its normalised fp32 O and lse, and the log-sum-exp combine of
+//     section 8 of the same page merges them into O through a row map.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
