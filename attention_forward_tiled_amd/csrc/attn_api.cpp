@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -70,15 +71,18 @@ size_t plan_bytes(int64_t batch) {
   return 256 + align256((size_t)(batch + 1) * sizeof(int32_t)) + align256(kMaxStreamWG * sizeof(int32_t));
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; callers may race, and all of
+// them store the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    if (const int c = cache[dev].load(std::memory_order_relaxed); c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64 && n > 0) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
