@@ -26,6 +26,8 @@ CUS = 256
 # ------------------------------------------------------------------ shared helpers
 
 def swz_prefill(D, row):
+    # (the d = 256 narrow kernel XORs by 2 (row % 16) instead; any mask below the row's
+    # chunk count only permutes the chunks of a row, so the sources checked are the same)
     row = np.asarray(row)
     if D == 64:
         k = (row >> 1) & 7
