@@ -194,3 +194,37 @@ def test_tail_split_policy(case, splits):
     need = attn_prefill_workspace_bytes(q, num_heads_kv=case.heads_kv, seqlen_k=case.seqlen_k, causal=case.causal,
                                         layout=case.layout, precise=case.precise)
     assert (need > 0) == splits, need
+
+
+BAD_ID_SPLIT = [
+    (P("split_bf16_d128_paged_bad_ids", 2, 8, 2, 100, 640, 128, "bf16", False, "paged",
+       seqlens_k=(640, 400)), 3),
+    (P("split_f16_d256_paged_bad_ids", 2, 6, 2, 200, 640, 256, "f16", False, "paged",
+       seqlens_k=(640, 400)), 4),
+]
+
+
+@pytest.mark.parametrize("case,parts", BAD_ID_SPLIT, ids=lambda x: getattr(x, "name", str(x)))
+def test_tail_split_invalid_page_ids_are_left_out(case, parts):
+    # a page id outside [0, num_blocks) drops that page's 64 keys in whichever part holds
+    # it; non-causal, so the expected result is the oracle on the table without those pages
+    import dataclasses
+    inp = make_prefill_inputs(case, seed=15)
+    nb = inp.k.shape[0]
+    bad = inp.block_table.copy()
+    bad[0, 3] = -1
+    bad[1, 5] = nb + 7
+    say(f"tail split parity with invalid page ids {case.name}, {parts} parts")
+    O, _ = gpu_prefill(dataclasses.replace(inp, block_table=bad), kv_splits=parts)
+    keep0 = [j for j in range(10) if j != 3]
+    keep1 = [j for j in range(7) if j != 5]
+    table = inp.block_table.copy()
+    table[:2] = 0
+    table[0, :len(keep0)] = inp.block_table[0, keep0]
+    table[1, :len(keep1)] = inp.block_table[1, keep1]
+    lens = inp.seqlens_k.copy()
+    lens[:2] -= 64
+    Oref, _ = oracle_prefill(dataclasses.replace(inp, block_table=table, seqlens_k=lens))
+    err = max_abs_err(O, Oref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= tolerance(case)
