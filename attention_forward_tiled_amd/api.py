@@ -83,6 +83,8 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     _need(q, "q", (torch.float16, torch.bfloat16))
     _need(k, "k", (q.dtype,))
     _need(v, "v", (q.dtype,))
+    if k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("k and v must be 4-D tensors of the same shape")
     if layout not in _LAYOUT:
         raise ValueError("layout must be 'bshd' or 'bhsd'")
     if cu_seqlens_q is not None:
@@ -99,10 +101,14 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     else:
         B, Hq, Sq, d = q.shape
     paged = block_table is not None
+    if k.shape[3] != d:
+        raise ValueError("k and v must have the head size of q")
     if paged:
         _need(block_table, "block_table", (torch.int32,))
         if seqlens_k is None:
             raise ValueError("paged K/V needs seqlens_k")
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [batch, max_blocks_per_seq]")
         num_blocks, page, Hkv = k.shape[0], k.shape[1], k.shape[2]
         if page != _lib.ATTN_PAGE_SIZE:
             raise ValueError(f"pages must hold {_lib.ATTN_PAGE_SIZE} tokens")
@@ -110,6 +116,8 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
         Sk = seqlen_k if seqlen_k is not None else max_blocks * _lib.ATTN_PAGE_SIZE
     else:
         num_blocks = max_blocks = 0
+        if k.shape[0] != B:
+            raise ValueError("dense K/V must have the batch of q")
         if layout == "bshd":
             Sk, Hkv = k.shape[1], k.shape[2]
         else:
@@ -118,6 +126,8 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
             raise ValueError("dense K/V: seqlen_k must equal the K/V row count")
     if seqlens_k is not None:
         _need(seqlens_k, "seqlens_k", (torch.int32,))
+        if seqlens_k.numel() != B:
+            raise ValueError("seqlens_k must hold one length per sequence")
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     _need(out, "out", tuple(_DT))
@@ -168,6 +178,39 @@ def attn_decode_workspace_bytes(batch: int, num_heads_q: int, num_splits: int, h
     return int(_lib.load().attn_decode_workspace_bytes(batch, num_heads_q, num_splits, head_dim))
 
 
+def _decode_shapes(q, k_cache, v_cache, block_table, seqlens_k):
+    """(B, Hq, Hkv, d, num_blocks) of a decode call, after checking that the tensors agree."""
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    _need(k_cache, "k_cache", (q.dtype,))
+    _need(v_cache, "v_cache", (q.dtype,))
+    _need(block_table, "block_table", (torch.int32,))
+    _need(seqlens_k, "seqlens_k", (torch.int32,))
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_blocks, 64, Hkv, d] of the same shape")
+    num_blocks, page, Hkv, d = k_cache.shape
+    if page != _lib.ATTN_PAGE_SIZE:
+        raise ValueError(f"pages must hold {_lib.ATTN_PAGE_SIZE} tokens")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+    B = block_table.shape[0]
+    if seqlens_k.numel() != B:
+        raise ValueError("seqlens_k must hold one length per sequence")
+    if B and q.numel() % (B * d) != 0:
+        raise ValueError("q must hold batch x num_heads_q x head_dim elements")
+    Hq = q.numel() // (B * d) if B else 0
+    return B, Hq, Hkv, d, num_blocks
+
+
+def _decode_outputs(out, lse, B, Hq, d):
+    _need(out, "out", tuple(_DT))
+    if out.numel() != B * Hq * d:
+        raise ValueError("out must hold batch x num_heads_q x head_dim elements")
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,))
+        if lse.numel() != B * Hq:
+            raise ValueError("lse must hold batch x num_heads_q elements")
+
+
 def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     block_table: torch.Tensor, seqlens_k: torch.Tensor, *, max_seqlen_k: int,
                     num_splits: int, out: Optional[torch.Tensor] = None,
@@ -175,21 +218,14 @@ def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                     workspace: Optional[torch.Tensor] = None, scale: float = 0.0,
                     out_round: str = "rtne", stream=None) -> torch.Tensor:
     """Split-KV decode. q: [B, Hq, d] (or any shape with B*Hq*d elements in that order)."""
-    _need(q, "q", (torch.float16, torch.bfloat16))
-    _need(k_cache, "k_cache", (q.dtype,))
-    _need(v_cache, "v_cache", (q.dtype,))
-    _need(block_table, "block_table", (torch.int32,))
-    _need(seqlens_k, "seqlens_k", (torch.int32,))
-    num_blocks, page, Hkv, d = k_cache.shape
-    if page != _lib.ATTN_PAGE_SIZE:
-        raise ValueError(f"pages must hold {_lib.ATTN_PAGE_SIZE} tokens")
-    B = block_table.shape[0]
-    Hq = q.numel() // (B * d) if B else 0
+    B, Hq, Hkv, d, num_blocks = _decode_shapes(q, k_cache, v_cache, block_table, seqlens_k)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _decode_outputs(out, lse, B, Hq, d)
     need = attn_decode_workspace_bytes(B, Hq, num_splits, d) if B else 0
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", (torch.uint8,))
     a = _lib.DecodeArgs(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -208,17 +244,8 @@ def attn_decode_fwd_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     Same arguments as attn_decode_fwd, but ``out`` must be passed (this call allocates
     nothing, here or in the library). Calls that overlap on one device race on the
     shared scratch; calls ordered on one stream do not."""
-    _need(q, "q", (torch.float16, torch.bfloat16))
-    _need(k_cache, "k_cache", (q.dtype,))
-    _need(v_cache, "v_cache", (q.dtype,))
-    _need(block_table, "block_table", (torch.int32,))
-    _need(seqlens_k, "seqlens_k", (torch.int32,))
-    _need(out, "out", tuple(_DT))
-    num_blocks, page, Hkv, d = k_cache.shape
-    if page != _lib.ATTN_PAGE_SIZE:
-        raise ValueError(f"pages must hold {_lib.ATTN_PAGE_SIZE} tokens")
-    B = block_table.shape[0]
-    Hq = q.numel() // (B * d) if B else 0
+    B, Hq, Hkv, d, num_blocks = _decode_shapes(q, k_cache, v_cache, block_table, seqlens_k)
+    _decode_outputs(out, lse, B, Hq, d)
     a = _lib.DecodeArgs(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
         _ptr(lse), None, 0, B, Hq, Hkv, d, num_blocks, block_table.shape[1], int(max_seqlen_k),
@@ -234,9 +261,12 @@ def attn_splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, *,
     """Merge partials: partial_o [B, H, S, d] fp32, partial_lse [B, H, S] fp32 -> [B, H, d]."""
     _need(partial_o, "partial_o", (torch.float32,))
     _need(partial_lse, "partial_lse", (torch.float32,))
+    if partial_o.dim() != 4 or tuple(partial_lse.shape) != tuple(partial_o.shape[:3]):
+        raise ValueError("partial_o must be [B, H, S, d] and partial_lse [B, H, S]")
     B, H, S, d = partial_o.shape
     if out is None:
         out = torch.empty((B, H, d), dtype=out_dtype, device=partial_o.device)
+    _decode_outputs(out, lse, B, H, d)
     a = _lib.CombineArgs(_ptr(partial_o), _ptr(partial_lse), _ptr(out), _ptr(lse), B, H, S, d,
                          _DT[out.dtype], _round(out_round))
     _check(_lib.load().attn_splitkv_combine(ctypes.byref(a), _stream(stream)))
