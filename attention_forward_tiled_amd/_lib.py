@@ -65,6 +65,7 @@ class DeviceInfo(ctypes.Structure):
 
 
 _LIB = None
+POISON_LIB_PATH = os.path.join(HERE, "libattn_poison.so")   # debug build: LDS filled with NaN first
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -72,6 +73,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _LIB
     if _LIB is not None:
         return _LIB
+    _LIB = open_library(path)
+    return _LIB
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library (libattn.so, or the LDS-poisoning debug build) with the
+    prototypes of include/attn.h; raise if it is missing or its ABI version differs."""
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is not built; run `python -m attention_forward_tiled_amd.build` "
@@ -98,8 +106,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_device_info.argtypes = [_i32, ctypes.POINTER(DeviceInfo)]
     lib.attn_device_info.restype = ctypes.c_int
     if lib.attn_abi_version() != ATTN_ABI_VERSION:
-        raise RuntimeError(f"libattn.so ABI version {lib.attn_abi_version()} != {ATTN_ABI_VERSION}")
-    _LIB = lib
+        raise RuntimeError(f"{os.path.basename(path)} ABI version {lib.attn_abi_version()} != {ATTN_ABI_VERSION}")
     return lib
 
 

@@ -4,7 +4,10 @@
 
 Every HIP source is compiled for gfx950 only. Packed fp32 VALU instructions are
 disabled on purpose (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
-Objects go to ``_build/``; the shared library lands next to this file.
+Objects go to ``_build/``; the shared library lands next to this file. A second,
+debug library, ``libattn_poison.so`` (objects in ``_build/poison``), is the same code
+compiled with ``-DATTN_POISON_LDS=1``: every kernel first fills its LDS with NaN bit
+patterns, so that a test run against it shows any read of LDS that nothing wrote.
 
 The kernels issue their global->LDS copies (global_load_lds_dwordx4) from inline asm
 that sets m0, the LDS destination register, without the compiler knowing (the
@@ -30,6 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libattn.so")
+OUT_POISON = os.path.join(HERE, "libattn_poison.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["attn_api.cpp", "prefill.hip", "decode.hip"]
 ARCH = "gfx950"
@@ -80,9 +84,9 @@ def check_m0(asm: str) -> list:
     return bad
 
 
-def _compile(src: str, build_dir: str = BUILD) -> str:
+def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(src, []), "-save-temps=obj", "-x", "hip", "-c",
+    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(src, []), *defines, "-save-temps=obj", "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=build_dir)
     noise = "'-packed-fp32-ops' is not a recognized feature"
@@ -132,11 +136,11 @@ def kernel_resources(asm: str) -> dict:
     return out
 
 
-def compile_all(build_dir: str = BUILD, jobs: int = 4) -> list:
+def compile_all(build_dir: str = BUILD, jobs: int = 4, defines: tuple = ()) -> list:
     """Compile every source into `build_dir` and check the m0 invariant of its assembly."""
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda src: _compile(src, build_dir), SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
     for src in SOURCES:
         bad = check_m0(device_asm(src, build_dir))
         if bad:
@@ -145,20 +149,29 @@ def compile_all(build_dir: str = BUILD, jobs: int = 4) -> list:
     return objs
 
 
-def build(jobs: int = 4, verbose: bool = True) -> str:
-    objs = compile_all(BUILD, jobs)
-    tmp = OUT + ".tmp"
+def _link(objs: list, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
+
+
+def build(jobs: int = 4, verbose: bool = True, poison: bool = True) -> str:
+    """Build libattn.so and (poison=True) the LDS-poisoning debug library beside it."""
+    out = _link(compile_all(BUILD, jobs), OUT, verbose)
+    if poison:
+        _link(compile_all(os.path.join(BUILD, "poison"), jobs, ("-DATTN_POISON_LDS=1",)), OUT_POISON, verbose)
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
-    build(ap.parse_args().jobs)
+    ap.add_argument("--no-poison", action="store_true", help="skip the LDS-poisoning debug library")
+    a = ap.parse_args()
+    build(a.jobs, poison=not a.no_poison)

@@ -172,6 +172,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)(p);
 }
 
+// Debug builds: fill BYTES of LDS with all-ones words (NaN as fp16, bf16 and fp32) and
+// wait for every thread, before the kernel's first copy into LDS.
+template <int BYTES>
+__device__ __forceinline__ void poison_lds(void* lds) {
+  uint32_t* w = static_cast<uint32_t*>(lds);
+  for (int i = threadIdx.x; i < BYTES / 4; i += blockDim.x) w[i] = 0xFFFFFFFFu;
+  __syncthreads();
+}
+
 // global_load_lds_dwordx4 with a per-lane 64-bit address: lane l's 16 bytes land at LDS
 // byte lds + 16 * l. Issued from inline asm so that the compiler does not fence LDS reads
 // of the other stage on it; completion is awaited explicitly (vmcnt) before the barrier

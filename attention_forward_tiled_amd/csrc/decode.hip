@@ -115,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
   static_assert(NST >= 2 && (NST - 2) * 2 * NIW < 64, "ring depth");
   static_assert(kWaves * 16 * OSTR * 4 + 2 * kWaves * 16 * 4 <= NST * 2 * TILE_B, "merge buffer");
   __shared__ __align__(16) char ring[NST * 2 * TILE_B];   // [stage][K, V][64 rows][D]
+  if constexpr (kPoisonLds) poison_lds<sizeof(ring)>(ring);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -314,6 +315,7 @@ __device__ __forceinline__ int seq_pages(const DecodeParams& p, int b) {
 // chunk, nwk}.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p) {
   __shared__ int part[1024];
+  if constexpr (kPoisonLds) poison_lds<sizeof(part)>(part);
   const int t = threadIdx.x;
   const int per = (p.batch + 1023) / 1024;
   const int b0 = min(t * per, p.batch), b1 = min(b0 + per, p.batch);
@@ -379,6 +381,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(const DecodePar
   static_assert(3 * DB * 1024 + 2 * 3 * 64 * 4 <= STAGE_B, "merge buffer");
   static_assert(QIW * kWaves * 1024 >= 16 * ROWB, "Q block");
   __shared__ __align__(16) char ring[NST * STAGE_B];   // [stage][K tile, V tile, Q block]
+  if constexpr (kPoisonLds) poison_lds<sizeof(ring)>(ring);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;

@@ -4,7 +4,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Debug builds (compiled with -DATTN_POISON_LDS=1, as libattn_poison.so) fill each
+// kernel's LDS with NaN bit patterns before its first use, so that a read of LDS that no
+// copy or store wrote reaches the output as NaN. Release builds compile none of it.
+#ifndef ATTN_POISON_LDS
+#define ATTN_POISON_LDS 0
+#endif
+
 namespace attn {
+
+constexpr bool kPoisonLds = ATTN_POISON_LDS != 0;
 
 enum DType { kF16 = 0, kBF16 = 1, kF32 = 2 };
 

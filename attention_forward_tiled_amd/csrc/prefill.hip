@@ -98,6 +98,7 @@ void prefill_kernel(const PrefillParams p) {
   constexpr int TILE = kPage * D;       // elements per K (or V) tile
   constexpr int ROWB = D * 2;           // bytes per LDS row
   __shared__ __align__(16) uint16_t smem[NG * 2 * 2 * TILE];   // [group][2 stages][K, V][TILE]
+  if constexpr (kPoisonLds) poison_lds<sizeof(smem)>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int grp = tid / (64 * NW);                              // key-range group
@@ -566,6 +567,7 @@ void prefill_narrow_kernel(const PrefillParams p) {
   constexpr int TILE = kPage * D;
   constexpr int ROWB = D * 2;
   __shared__ __align__(16) uint16_t smem[2 * 2 * TILE];   // [2 stages][K, V][TILE]
+  if constexpr (kPoisonLds) poison_lds<sizeof(smem)>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;

@@ -28,6 +28,14 @@ def test_header_symbols_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_poison_build_exports_the_same_symbols():
+    # the LDS-poisoning debug build is the same source compiled with one define
+    dbg = _lib.open_library(_lib.POISON_LIB_PATH)
+    for n in header_functions():
+        assert hasattr(dbg, n), n
+    assert dbg.attn_abi_version() == _lib.ATTN_ABI_VERSION
+
+
 def test_abi_version(lib):
     assert lib.attn_abi_version() == _lib.ATTN_ABI_VERSION
 
