@@ -19,7 +19,9 @@ bf16, key lengths U[1024, 65536], 16 splits) measured the same way (10 warmup
 launches, 10 repetitions of 50), a roofline object for the dominant kernel of each,
 the parity of the timed outputs against the fp64 oracle on a sample, the oracle
 itself timed on the host cores (cpu_baseline), and the device facts the peaks are
-derived from.
+derived from. A failing parity check withholds the value (null) and exits non-zero;
+--debug-mismatch N lists the N largest deviations from the oracle, --report PATH
+writes the line to a file as well.
 """
 from __future__ import annotations
 
@@ -222,10 +224,11 @@ class PrefillWorkload:
         value = frac * self.work() / sec / 1e12
         got = self.out.float().cpu().numpy().astype(np.float64)
         got = got[:, rows] if c.layout == "bshd" else got[:, :, rows]
-        err = float(np.abs(got - O).max())
         text = (f"oracle on {rows.size} of {c.seqlen_q} query rows x all {c.batch * c.heads_q} "
                 f"(sequence, head) pairs ({100 * frac:.2f}% of the visible pairs), {reps} rep(s)")
-        return value, sec, text, err
+        names = ("seq", "row", "head", "col") if c.layout == "bshd" else ("seq", "head", "row", "col")
+        maps = tuple(rows if nm == "row" else None for nm in names)
+        return value, sec, text, (got, O, names, maps)
 
 
 class DecodeWorkload:
@@ -305,10 +308,9 @@ class DecodeWorkload:
         sec = t_total / reps
         nbytes = 2 * int(inp.seqlens_k[seqs].sum()) * c.heads_kv * c.head_dim * 2
         got = self.out.float().cpu().numpy().astype(np.float64)[seqs]
-        err = float(np.abs(got - O[:, 0]).max())
         text = (f"oracle on {len(seqs)} of {c.batch} sequences (key lengths "
                 f"{inp.seqlens_k[seqs].tolist()}), all heads, {reps} rep(s)")
-        return nbytes / sec / 1e9, sec, text, err
+        return nbytes / sec / 1e9, sec, text, (got, O[:, 0], ("seq", "head", "col"), (np.array(seqs), None, None))
 
 
 def make_workload(name, seed):
@@ -404,14 +406,28 @@ def measure(wl, steps, warmup, reps, spinup_ms, torch, dev):
     return ms, stats, roofline(wl, kernel_ms, dev), spin
 
 
-def parity_and_baseline(wl, cpu_seconds, no_cpu):
+def worst_samples(got, ref, n, names, maps):
+    """The n entries with the largest |got - ref|, worst first: their index along each named
+    axis (through `maps` back to the whole output where the sample took a subset) and both
+    values."""
+    err = np.abs(got - ref)
+    out = []
+    for f in np.argsort(err, axis=None, kind="stable")[::-1][:n]:
+        idx = np.unravel_index(f, err.shape)
+        where = {nm: int(m[i]) if m is not None else int(i) for nm, m, i in zip(names, maps, idx)}
+        out.append({**where, "got": float(got[idx]), "expected": float(ref[idx]), "abs_err": float(err[idx])})
+    return out
+
+
+def parity_and_baseline(wl, cpu_seconds, no_cpu, debug_mismatch=0):
     """Parity of the timed output on the oracle sample, and the oracle timed on it."""
     unit, _ = wl.unit()
     if not wl.finite():
         return None, {"max_abs_err": None, "pass": False, "checked": "output has NaN/inf (rows left unwritten)"}
     if no_cpu:
         return None, None
-    cv, sec, text, err = wl.cpu_sample(cpu_seconds)
+    cv, sec, text, (got, ref, names, maps) = wl.cpu_sample(cpu_seconds)
+    err = float(np.abs(got - ref).max())
     host = host_facts()
     cpu = {"value": round(cv, 6), "unit": unit, "cores": host["blas_threads"], "kind": "oracle",
            "sample": text, "seconds": round(sec, 3), "host_cpu_count": host["cpu_count"],
@@ -421,6 +437,10 @@ def parity_and_baseline(wl, cpu_seconds, no_cpu):
     parity = {"max_abs_err": err, "tol": tol, "pass": bool(err <= tol),
               "checked": "whole output finite (NaN-filled before the first launch); timed output vs the "
                          "fp64 oracle on the cpu_baseline sample"}
+    if debug_mismatch > 0:
+        parity["worst"] = worst_samples(got, ref, debug_mismatch, names, maps)
+        for w in parity["worst"]:
+            print(f"# {wl.case.name} mismatch: {w}", file=sys.stderr, flush=True)
     return cpu, parity
 
 
@@ -442,6 +462,10 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (HBM counter calibration)")
+    ap.add_argument("--debug-mismatch", type=int, default=0, metavar="N",
+                    help="add the N largest deviations from the oracle (index, value, expected) to "
+                         "each parity object and print them")
+    ap.add_argument("--report", metavar="PATH", help="also write the JSON line, indented, to PATH")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -476,7 +500,7 @@ def main(argv=None):
         dunit, dscale = dw.unit()
         dvalue = dw.work() / (dms * 1e-3) / dscale
         print(f"# {args.decode_workload}: {dms:.5f} ms per step", file=sys.stderr, flush=True)
-        dcpu, dpar = parity_and_baseline(dw, 2.0, args.no_cpu_baseline)
+        dcpu, dpar = parity_and_baseline(dw, 2.0, args.no_cpu_baseline, args.debug_mismatch)
         ok = dpar is None or dpar["pass"]
         dec = {"workload": dw.case.name, "value": round(dvalue, 1) if ok else None, "unit": dunit,
                "ms_per_step": round(dms, 6), "timing": dstats,
@@ -490,7 +514,7 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    cpu, parity = parity_and_baseline(wl, args.cpu_seconds, args.no_cpu_baseline)
+    cpu, parity = parity_and_baseline(wl, args.cpu_seconds, args.no_cpu_baseline, args.debug_mismatch)
     ok = parity is None or parity["pass"]
     line = {
         "metric": METRIC,
@@ -503,6 +527,9 @@ def main(argv=None):
         "host": host_facts(),
     }
     print(json.dumps(line), flush=True)
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(line, f, indent=1)
     dec_ok = dec is None or dec["parity"] is None or dec["parity"]["pass"]
     return 0 if (ok and dec_ok) else 1
 

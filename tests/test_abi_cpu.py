@@ -246,3 +246,21 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU only" in (r.stdout + r.stderr)
     assert r.stdout.strip() == "" or not r.stdout.lstrip().startswith("{")
+
+
+def test_bench_worst_samples_names_the_deviations():
+    # --debug-mismatch: the largest deviations, worst first, with each index mapped back to
+    # the whole output where the parity sample took a subset of the query rows
+    import sys
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    from bench import worst_samples
+    rows = np.array([3, 40, 77])
+    ref = np.zeros((2, 3, 4, 8))           # [seq, sampled row, head, col]
+    got = ref.copy()
+    got[1, 2, 3, 5] = 0.5
+    got[0, 1, 0, 0] = -0.25
+    got[1, 0, 2, 7] = 1e-3
+    w = worst_samples(got, ref, 2, ("seq", "row", "head", "col"), (None, rows, None, None))
+    assert [(x["seq"], x["row"], x["head"], x["col"]) for x in w] == [(1, 77, 3, 5), (0, 40, 0, 0)]
+    assert w[0]["got"] == 0.5 and w[0]["expected"] == 0.0 and w[1]["abs_err"] == 0.25
