@@ -75,3 +75,52 @@ def test_hot_kernels_fit_their_register_budgets(built):
         assert r["vgpr_spill"] == 0 and r["scratch"] == 0, (k, r)
     for k, r in {**pre, **dec}.items():
         assert r["lds"] <= 160 * 1024, (k, r)
+
+
+def _kernel_bodies(asm):
+    """{mangled kernel name: its instructions, in order} from gfx950 assembly."""
+    out, name, body = {}, None, []
+    for line in asm.split("\n"):
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            name, body = m.group(1), []
+            continue
+        if name is None:
+            continue
+        if line.startswith(".Lfunc_end"):
+            out[name], name = body, None
+            continue
+        t = line.strip()
+        if t and not t.startswith((";", ".")):
+            body.append(t.split()[0])
+    return out
+
+
+@pytest.fixture(scope="module")
+def built_poison(tmp_path_factory):
+    d = str(tmp_path_factory.mktemp("asm_poison"))
+    build.compile_all(d, jobs=3, defines=("-DATTN_POISON_LDS=1",))
+    return d
+
+
+def test_poison_build_fills_lds_before_any_copy_or_read(built, built_poison):
+    """In the LDS-poisoning debug build every kernel that uses LDS stores to it and passes
+    a barrier before its first global->LDS copy or LDS read; the LDS sizes and the set of
+    kernels are those of the release build."""
+    for src in ("prefill.hip", "decode.hip"):
+        rel = build.kernel_resources(build.device_asm(src, built))
+        asm = build.device_asm(src, built_poison)
+        dbg = build.kernel_resources(asm)
+        assert set(dbg) == set(rel), src
+        bodies = _kernel_bodies(asm)
+        with_lds = [k for k, r in dbg.items() if r.get("lds", 0) > 0]
+        assert with_lds, src
+        for k in with_lds:
+            assert dbg[k]["lds"] == rel[k]["lds"], k
+            ins = bodies[k]
+            first = next(i for i, x in enumerate(ins)
+                         if x.startswith(("ds_read", "global_load_lds", "buffer_load")) and
+                         (x.startswith("ds_read") or "lds" in x))
+            head = ins[:first]
+            assert any(x.startswith("ds_write") for x in head), k
+            assert "s_barrier" in head, k
