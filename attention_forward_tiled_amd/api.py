@@ -146,6 +146,8 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     lib = _lib.load()
     if workspace is None and int(kv_splits) != 1:
         need = int(lib.attn_prefill_workspace_bytes(ctypes.byref(a)))
+        if need == 0 and int(kv_splits) >= 2:
+            need = 256        # the C ABI takes a workspace with every kv_splits >= 2, split or not
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:

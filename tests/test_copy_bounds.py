@@ -559,3 +559,36 @@ def test_copy_base_survives_bit31_of_the_low_word():
     # the unwidened composition (what the check guards against) would differ
     lo = int(readfirstlane(0x7F12_8000_0000))
     assert lo < 0 and ((0x7F12 << 32) | (lo & 0xFFFF_FFFF_FFFF_FFFF)) != 0x7F12_8000_0000
+
+
+def test_random_sweep_addresses_in_bounds():
+    """Every shape of the seeded random parity sweep (tests/test_random_shapes_gpu.py)
+    through the same address models, before any of it runs on a device: the prefill
+    launch form the host picks (and, for a forced split of a launch that qualifies, the
+    split units with every item in the tail), packed queries, and both decode kernels."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from test_random_shapes_gpu import N_DECODE, N_PACKED, N_PREFILL, draw_decode, draw_packed, draw_prefill
+    for i in range(N_PREFILL):
+        c, splits = draw_prefill(i)
+        D, B, Hq, Hkv, Sq, Sk = c.head_dim, c.batch, c.heads_q, c.heads_kv, c.seqlen_q, c.seqlen_k
+        paged = c.kv == "paged"
+        check_prefill(D, B, Hq, Hkv, Sq, Sk, c.causal, paged, c.layout, c.seqlens_k)
+        if splits < 2 or c.precise or c.layout != "bshd":
+            continue
+        NG, NW, PAIR, bq = prefill_form(D, c.causal, Hq // Hkv, Sq, Sk, B, Hkv)
+        items = -(-Sq // bq) * Hkv * B
+        few = 2 * items <= CUS and (NG == 2 or D == 256) and not PAIR
+        if not c.causal or few:
+            check_tail_split(D, B, Hq, Hkv, Sq, Sk, items, splits, paged, c.seqlens_k, causal=c.causal)
+    for i in range(N_PACKED):
+        c, q_lens = draw_packed(i)
+        cu = np.concatenate([[0], np.cumsum(q_lens)])
+        check_prefill(c.head_dim, c.batch, c.heads_q, c.heads_kv, c.seqlen_q, c.seqlen_k, c.causal,
+                      c.kv == "paged", lens=c.seqlens_k, cu=cu)
+    for i in range(N_DECODE):
+        c, splits = draw_decode(i)
+        check_decode_split(c.head_dim, c.lengths_fixed, c.heads_q, c.heads_kv, 1)
+        if splits >= 2:
+            check_decode_stream(c.head_dim, c.lengths_fixed, c.heads_q, c.heads_kv, splits)
