@@ -731,15 +731,29 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
 #pragma unroll
   for (int msk = 1; msk < 64; msk <<= 1) den = wave_sum_xor(den, msk);
 
+  // The partials of CH splits are loaded together, so that their latencies overlap
+  // (a load per split behind a branch on its weight would wait for each in turn). A split
+  // of weight 0 (no key; its O_s may never have been written) is read like the others,
+  // inside the workspace, and then left out by a select, so the sum is the same, term by
+  // term and in the same order, as skipping it.
+  constexpr int CH = 8;
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ws = __shfl(w, s, 64);
-    if (ws == 0.f) continue;                      // empty split: its O_s is never read
-    const float* src = p.part_o + ((int64_t)pair * S + s) * D + lane * PER;
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float v[CH][PER], ws[CH];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = fmaf(ws, src[e], o[e]);
+    for (int k = 0; k < CH; ++k) {
+      const int s = min(s0 + k, S - 1);
+      ws[k] = s0 + k < S ? __shfl(w, s, 64) : 0.f;
+      const float* src = p.part_o + ((int64_t)pair * S + s) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[k][e] = src[e];
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = ws[k] != 0.f ? fmaf(ws[k], v[k][e], o[e]) : o[e];
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int64_t ob = obase + lane * PER;
