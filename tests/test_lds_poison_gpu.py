@@ -137,3 +137,32 @@ def test_decode_invalid_page_ids_read_only_written_lds(use_poison, splits):
         lens[b] -= 64
     Oref, _ = oracle_decode(dataclasses.replace(inp, block_table=table, seqlens_k=lens))
     assert max_abs_err(O, Oref) <= TOL[case.dtype]
+
+
+@pytest.mark.parametrize("i", range(0, 96, 4))
+def test_random_prefill_reads_only_written_lds(use_poison, i):
+    # every fourth draw of the seeded random sweep, against the poisoned build
+    from test_random_shapes_gpu import draw_prefill
+    case, splits = draw_prefill(i)
+    say(f"random prefill, LDS poisoned {case.name}")
+    inp = make_prefill_inputs(case, seed=100 + i)
+    O, lse = gpu_prefill(inp, with_lse=True, kv_splits=splits)
+    Oref, lref = oracle_prefill(inp)
+    assert max_abs_err(O, Oref) <= tolerance(case)
+    fin = np.isfinite(lref)
+    assert (np.isneginf(lse) == ~fin).all()
+    assert np.abs(lse[fin] - lref[fin]).max(initial=0.0) <= lse_tolerance(case.dtype, case.precise)
+
+
+@pytest.mark.parametrize("i", range(0, 48, 4))
+def test_random_decode_reads_only_written_lds(use_poison, i):
+    from test_decode_gpu import gpu_decode
+    from test_random_shapes_gpu import draw_decode
+    case, splits = draw_decode(i)
+    say(f"random decode, LDS poisoned {case.name}")
+    inp = make_decode_inputs(case, seed=300 + i)
+    O, lse = gpu_decode(inp, splits, with_lse=True)
+    Oref, lref = oracle_decode(inp)
+    assert max_abs_err(O, Oref) <= TOL[case.dtype]
+    fin = np.isfinite(lref)
+    assert (np.isneginf(lse) == ~fin).all()
