@@ -10,11 +10,11 @@
 //   * A group of NW waves owns 32 * NW query rows that share one KV head: for a GQA
 //     group of G query heads it takes 32 * NW / G positions of every head of the group,
 //     so each K/V tile brought into LDS serves all G heads. Three launch forms (chosen
-//     on the host, see launch_one): eight waves / 256 rows for large launches (twice the
-//     rows per copied tile); two groups of four waves splitting one block's key tiles
-//     (merged through LDS) for causal launches with few blocks, optionally pairing a
-//     heavy and a light block per workgroup; otherwise four waves / 128 rows, two
-//     workgroups per CU.
+//     on the host, see launch_one): eight waves / 256 rows for large launches at
+//     d = 128 (twice the rows per copied tile); two groups of four waves splitting one
+//     block's key tiles (merged through LDS) for causal launches with few blocks,
+//     optionally pairing a heavy and a light block per workgroup; otherwise four waves /
+//     128 rows, two workgroups per CU (three at d = 64).
 //   * Each wave owns 32 rows. Scores are produced transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16: K comes from LDS as the A operand and Q stays in registers
 //     as the B operand for the whole kernel. The accumulator then holds, per lane, one
@@ -864,9 +864,12 @@ struct Form {
 template <int D, bool PRECISE>
 Form choose_form(const PrefillParams& p) {
   Form f;
-  if constexpr (D <= 128) {
+  if constexpr (D == 128) {
     // Large launches: eight-wave workgroups of 256 query rows share each K/V tile, as long
-    // as that still leaves at least four workgroups per CU.
+    // as that still leaves at least four workgroups per CU. (d = 64 keeps four-wave
+    // blocks, three workgroups per CU: its tile loop is bound by the softmax, and a third
+    // wave per SIMD hides more of it than shared copies save; 4.5-11% faster on four
+    // d = 64 shapes, causal and not, bit-equal.)
     // Causal MHA below 8192 keys keeps the four-wave blocks: an eight-wave block of G = 1
     // spans 256 positions, four of its tiles straddle the diagonal, and at these lengths
     // that costs more than the shared copies save (8% at 4096, even at 8192).
@@ -963,7 +966,8 @@ hipError_t plan_one(const PrefillParams& p, int kv_splits, PrefillPlan* plan) {
     int occ = 1;
     hipError_t e;
     if constexpr (D == 256) e = resident_per_cu<D, 0, T>(&occ);
-    else e = (f.nw == 8 && !fill) ? resident_per_cu<D, 8, T>(&occ) : resident_per_cu<D, 4, T>(&occ);
+    else if constexpr (D == 128) e = (f.nw == 8 && !fill) ? resident_per_cu<D, 8, T>(&occ) : resident_per_cu<D, 4, T>(&occ);
+    else e = resident_per_cu<D, 4, T>(&occ);
     if (e != hipSuccess) return e;
     const int64_t cap = (int64_t)occ * std::max(p.cus, 1);
     const int64_t tail = fill ? f.items : f.items % cap;
@@ -1005,7 +1009,7 @@ hipError_t launch_one(const PrefillParams& p0, const PrefillPlan& plan, hipStrea
       hipLaunchKernelGGL((prefill_narrow_kernel<D, T>), dim3((unsigned)blocks), dim3(512), 0, stream, q);
       return hipGetLastError();
     } else {
-      if constexpr (D <= 128) {
+      if constexpr (D == 128) {
         if (f.nw == 8) return launch_ng<D, 1, 8, T, PRECISE>(q, blocks, stream);
       }
       return launch_ng<D, 1, 4, T, PRECISE>(q, blocks, stream);

@@ -84,7 +84,7 @@ def assert_inside(off, zero, n_elems, what):
 
 def prefill_form(D, causal, G, Sq, Sk, B, Hkv):
     """(NG, NW, PAIR, bq) chosen by the host for a launch (launch_one)."""
-    if D <= 128:
+    if D == 128:
         diag_heavy = causal and G == 1 and Sk < 8192
         bq = 256 // G
         blocks8 = -(-Sq // bq) * Hkv * B
@@ -211,7 +211,8 @@ PREFILL_CASES = [
     (128, 1, 32, 8, 2048, 2048, True, True, "bshd", None, ()),           # paired two-group form
     (128, 1, 32, 8, 2080, 2080, True, True, "bshd", None, ((0, 5, -7),)),  # odd block count
     (128, 4, 16, 4, 512, 4096, True, True, "bshd", (4096, 4000, 3999, 1), ()),
-    (64, 4, 64, 32, 1024, 1024, True, True, "bshd", None, ()),           # eight-wave form, d = 64
+    (64, 4, 64, 32, 1024, 1024, True, True, "bshd", None, ()),           # d = 64: four-wave blocks
+    (128, 4, 64, 32, 1024, 1024, True, True, "bshd", None, ()),          # the same, eight-wave form
     (128, 2, 12, 4, 4100, 4100, True, True, "bshd", (4100, 3000), ((1, 3, 99999),)),
     (256, 1, 8, 8, 3000, 1000, False, False, "bshd", None, ()),
 ]

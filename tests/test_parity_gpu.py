@@ -200,21 +200,26 @@ def test_prefill_wide_groups(case, splits):
 
 
 EIGHT_WAVE = [
-    P("f16_d64_gqa2_causal_paged_1024wg8", 4, 64, 32, 1024, 1024, 64, "f16", True, "paged"),
+    P("f16_d128_gqa2_causal_paged_1024wg8", 4, 64, 32, 1024, 1024, 128, "f16", True, "paged"),
     P("bf16_d128_noncausal_dense_1024wg8", 8, 32, 8, 1000, 1100, 128, "bf16", False, "dense",
       seqlens_k=(1100, 1000, 999, 64, 1, 700, 1100, 130)),
     P("bf16_d128_gqa8_causal_paged_ragged_wg8", 2, 32, 4, 4100, 4100, 128, "bf16", True, "paged",
       seqlens_k=(4100, 3000)),
-    P("f16_d64_noncausal_dense_bhsd_cross_wg8", 4, 16, 16, 4100, 333, 64, "f16", False, "dense",
+    P("f16_d128_noncausal_dense_bhsd_cross_wg8", 4, 16, 16, 4100, 333, 128, "f16", False, "dense",
       layout="bhsd"),
     # group sizes that leave rows of a 256-row workgroup unused (G = 3: 85 positions x 3
     # heads; G = 6: 42 x 6) and a narrow one (G = 32: 8 positions x 32 heads)
     P("bf16_d128_gqa3_causal_paged_wg8", 3, 12, 4, 8200, 8200, 128, "bf16", True, "paged",
       seqlens_k=(8200, 5000, 7777)),
-    P("f16_d64_gqa6_noncausal_dense_wg8", 4, 24, 4, 5000, 700, 64, "f16", False, "dense"),
+    P("f16_d128_gqa6_noncausal_dense_wg8", 4, 24, 4, 5000, 700, 128, "f16", False, "dense"),
     P("bf16_d128_gqa32_causal_paged_wg8", 4, 64, 2, 1100, 1100, 128, "bf16", True, "paged"),
     # precise P (hi + lo products) with an fp32 output, in the eight-wave form
-    P("f16_d64_precise_f32out_dense_wg8", 4, 16, 16, 4096, 4096, 64, "f16", False, "dense",
+    P("f16_d128_precise_f32out_dense_wg8", 4, 16, 16, 4096, 4096, 128, "f16", False, "dense",
+      out_dtype="f32", precise=True),
+    # (not eight-wave) the same launch sizes at d = 64, which keeps four-wave blocks
+    P("f16_d64_gqa2_causal_paged_1024wg4", 4, 64, 32, 1024, 1024, 64, "f16", True, "paged"),
+    P("f16_d64_gqa6_noncausal_dense_wg4", 4, 24, 4, 5000, 700, 64, "f16", False, "dense"),
+    P("f16_d64_precise_f32out_dense_wg4", 4, 16, 16, 4096, 4096, 64, "f16", False, "dense",
       out_dtype="f32", precise=True),
     # (not eight-wave) causal MHA below 8192 keys: four-wave blocks, sampled rows
     P("bf16_d128_causal_mha_dense_4k_wg4", 2, 32, 32, 4096, 4096, 128, "bf16", True, "dense"),
@@ -268,7 +273,7 @@ VARLEN = [
     (P("bf16_d256_causal_paged_gqa2_varlen", 3, 4, 2, 300, 700, 256, "bf16", True, "paged",
        seqlens_k=(700, 65, 300)), (300, 1, 129)),
     # eight-wave form (max_seqlen_q 4096: 16 x 8 heads x 8 sequences = 1024 workgroups)
-    (P("f16_d64_noncausal_dense_varlen_wg8", 8, 8, 8, 4096, 1000, 64, "f16", False, "dense",
+    (P("f16_d128_noncausal_dense_varlen_wg8", 8, 8, 8, 4096, 1000, 128, "f16", False, "dense",
        seqlens_k=(200, 64, 1, 130, 700, 5, 64, 999)), (4096, 0, 1, 255, 256, 257, 1000, 3000)),
 ]
 
@@ -330,7 +335,10 @@ BAD_ID_CASES = [
     P("f16_d256_noncausal_paged_bad_ids", 2, 6, 2, 200, 640, 256, "f16", False, "paged",
       seqlens_k=(640, 400)),
     # eight-wave form: 32 x 8 heads x 4 sequences = 1024 workgroups
-    P("f16_d64_noncausal_paged_bad_ids_wg8", 4, 8, 8, 8192, 640, 64, "f16", False, "paged",
+    P("f16_d128_noncausal_paged_bad_ids_wg8", 4, 8, 8, 8192, 640, 128, "f16", False, "paged",
+      seqlens_k=(640, 400, 640, 64)),
+    # d = 64 (four-wave blocks at any size)
+    P("f16_d64_noncausal_paged_bad_ids_wg4", 4, 8, 8, 8192, 640, 64, "f16", False, "paged",
       seqlens_k=(640, 400, 640, 64)),
 ]
 
