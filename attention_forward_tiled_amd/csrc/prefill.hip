@@ -865,8 +865,11 @@ template <int D, bool PRECISE>
 Form choose_form(const PrefillParams& p) {
   Form f;
   if constexpr (D == 128) {
-    // Large launches: eight-wave workgroups of 256 query rows share each K/V tile, as long
-    // as that still leaves at least four workgroups per CU. (d = 64 keeps four-wave
+    // Eight-wave workgroups of 256 query rows share each K/V tile. They take every
+    // non-causal launch with at least one of them per CU, and every causal launch with at
+    // least one and a half per CU (dispatched heaviest first, that many balance the
+    // causal triangle; with one per CU the longest item sets the time and the two-group
+    // form below is faster). (d = 64 keeps four-wave
     // blocks, three workgroups per CU: its tile loop is bound by the softmax, and a third
     // wave per SIMD hides more of it than shared copies save; 4.5-11% faster on four
     // d = 64 shapes, causal and not, bit-equal.)
@@ -876,7 +879,8 @@ Form choose_form(const PrefillParams& p) {
     const bool diag_heavy = p.causal && p.group == 1 && p.seqlen_k < 8192;
     const int bq8 = 256 / p.group;
     const int64_t blocks8 = (int64_t)((p.seqlen_q + bq8 - 1) / bq8) * p.hkv * p.batch;
-    if (!diag_heavy && blocks8 >= 4 * (int64_t)std::max(p.cus, 1)) {
+    const int64_t cus = std::max(p.cus, 1);
+    if (!diag_heavy && (p.causal ? 2 * blocks8 >= 3 * cus : blocks8 >= cus)) {
       f.nw = 8; f.bq = bq8; f.blocks = f.items = blocks8;
       return f;
     }

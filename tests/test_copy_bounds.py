@@ -88,7 +88,7 @@ def prefill_form(D, causal, G, Sq, Sk, B, Hkv):
         diag_heavy = causal and G == 1 and Sk < 8192
         bq = 256 // G
         blocks8 = -(-Sq // bq) * Hkv * B
-        if not diag_heavy and blocks8 >= 4 * CUS:
+        if not diag_heavy and (2 * blocks8 >= 3 * CUS if causal else blocks8 >= CUS):
             return 1, 8, False, bq
     bq = 128 // G
     nq = -(-Sq // bq)

@@ -140,8 +140,9 @@ def test_prefill_deterministic():
     np.testing.assert_array_equal(a, b)
 
 
-# Launch forms (d <= 128, a device with 256 compute units): launches with at least 1024
-# eight-wave workgroups of 256 query rows take that form; otherwise causal launches of
+# Launch forms (d <= 128, a device with 256 compute units): at d = 128, non-causal launches
+# with at least 256 eight-wave workgroups of 256 query rows, and causal ones with at least
+# 384, take that form; otherwise causal launches of
 # fewer than 2048 four-wave workgroups split each workgroup's key range over two groups
 # (the small causal cases above), pairing a heavy and a light query block per workgroup
 # from 512 query blocks on, and the rest run one four-wave group per workgroup. The paired
