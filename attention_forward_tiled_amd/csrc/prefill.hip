@@ -869,13 +869,14 @@ Form choose_form(const PrefillParams& p) {
     // non-causal launch with at least one of them per CU, and every causal launch with at
     // least one and a half per CU (dispatched heaviest first, that many balance the
     // causal triangle; with one per CU the longest item sets the time and the two-group
-    // form below is faster). (d = 64 keeps four-wave
-    // blocks, three workgroups per CU: its tile loop is bound by the softmax, and a third
-    // wave per SIMD hides more of it than shared copies save; 4.5-11% faster on four
-    // d = 64 shapes, causal and not, bit-equal.)
+    // form below is faster).
     // Causal MHA below 8192 keys keeps the four-wave blocks: an eight-wave block of G = 1
     // spans 256 positions, four of its tiles straddle the diagonal, and at these lengths
-    // that costs more than the shared copies save (8% at 4096, even at 8192).
+    // that costs more than the shared copies save (8% at 4096 keys; from 8192 keys on the
+    // eight-wave form is ahead).
+    // d = 64 keeps four-wave blocks, three workgroups per CU: its tile loop is bound by
+    // the softmax, and a third wave per SIMD hides more of it than shared copies save
+    // (4.5-11% faster on four d = 64 shapes, causal and not, bit-equal).
     const bool diag_heavy = p.causal && p.group == 1 && p.seqlen_k < 8192;
     const int bq8 = 256 / p.group;
     const int64_t blocks8 = (int64_t)((p.seqlen_q + bq8 - 1) / bq8) * p.hkv * p.batch;
