@@ -215,6 +215,11 @@ PREFILL_CASES = [
     (128, 4, 64, 32, 1024, 1024, True, True, "bshd", None, ()),          # the same, eight-wave form
     (128, 2, 12, 4, 4100, 4100, True, True, "bshd", (4100, 3000), ((1, 3, 99999),)),
     (256, 1, 8, 8, 3000, 1000, False, False, "bshd", None, ()),
+    # eight-wave launches with one (non-causal) or one and a half (causal) items per CU
+    (128, 1, 16, 16, 4096, 4096, False, False, "bshd", None, ()),
+    (128, 1, 32, 8, 3072, 3072, True, True, "bshd", None, ((0, 7, -3),)),
+    (128, 2, 32, 8, 2048, 2048, True, True, "bshd", (2048, 1500), ()),
+    (128, 1, 48, 16, 4096, 4096, True, True, "bshd", None, ()),
 ]
 
 

@@ -222,6 +222,13 @@ EIGHT_WAVE = [
     P("f16_d64_gqa6_noncausal_dense_wg4", 4, 24, 4, 5000, 700, 64, "f16", False, "dense"),
     P("f16_d64_precise_f32out_dense_wg4", 4, 16, 16, 4096, 4096, 64, "f16", False, "dense",
       out_dtype="f32", precise=True),
+    # launches that take the eight-wave form with one (non-causal) or one and a half
+    # (causal) workgroups per CU: 256, 384, 512 and 784 items
+    P("bf16_d128_noncausal_dense_256items_wg8", 1, 16, 16, 4096, 4096, 128, "bf16", False, "dense"),
+    P("bf16_d128_causal_paged_384items_wg8", 1, 32, 8, 3072, 3072, 128, "bf16", True, "paged"),
+    P("f16_d128_causal_paged_ragged_512items_wg8", 2, 32, 8, 2048, 2048, 128, "f16", True, "paged",
+      seqlens_k=(2048, 1500)),
+    P("bf16_d128_gqa3_causal_paged_784items_wg8", 1, 48, 16, 4096, 4096, 128, "bf16", True, "paged"),
     # (not eight-wave) causal MHA below 8192 keys: four-wave blocks, sampled rows
     P("bf16_d128_causal_mha_dense_4k_wg4", 2, 32, 32, 4096, 4096, 128, "bf16", True, "dense"),
     P("bf16_d128_precise_f32out_paged_wg8", 2, 32, 8, 4096, 3000, 128, "bf16", False, "paged",
